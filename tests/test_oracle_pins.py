@@ -1,0 +1,357 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself:
+the blog's worked MLP example, closed forms, brute-force loops on tiny
+inputs, causal special cases, the sharded == unsharded invariant of the
+tensor-parallel method, and central finite differences."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import tp_layer_oracle as O
+from megatron_tensor_layer_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_params(rng, h, ffn, std=0.3):
+    shapes = {"Wq": (h, h), "Wk": (h, h), "Wv": (h, h), "bq": (h,), "bk": (h,), "bv": (h,),
+              "Wo": (h, h), "bo": (h,), "W1": (h, ffn), "b1": (ffn,), "W2": (ffn, h), "b2": (h,)}
+    return {k: rng.standard_normal(v) * std for k, v in shapes.items()}
+
+
+# ---------------------------------------------------------------------------
+# worked MLP example ('parallelism' blog, 'The MLP, with real numbers' and
+# 'The backward pass')
+# ---------------------------------------------------------------------------
+
+class TestWorkedExample:
+    g = _golden("worked_mlp_relu.json")
+    X = np.array(g["X"], float)
+    A = np.array(g["A"], float)
+    B = np.array(g["B"], float)
+
+    def test_unsharded_forward(self):
+        out, cache = O.mlp_branch_forward(self.X, self.A, 0.0, self.B, 0.0, act="relu")
+        np.testing.assert_array_equal(cache["U"], self.g["XA"])
+        np.testing.assert_array_equal(out, self.g["Z"])
+
+    def test_row_split_of_A_is_wrong(self):
+        # the page's counter-example: ReLU of per-row partial products
+        parts = [self.X[:, i:i + 1] @ self.A[i:i + 1, :] for i in range(2)]
+        np.testing.assert_array_equal(O.relu(parts[0]) + O.relu(parts[1]), self.g["row_split_wrong_relu_sum"])
+        assert not np.array_equal(O.relu(parts[0]) + O.relu(parts[1]), O.relu(self.X @ self.A))
+
+    def test_two_shards_forward_and_backward(self):
+        p = {"W1": self.A, "b1": np.zeros(4), "W2": self.B, "b2": np.zeros(2)}
+        ts = self.g["two_shards"]
+        dZ = np.array(self.g["dZ"], float)
+        partials, dx_parts = [], []
+        for r in range(2):
+            pr = {"W1": p["W1"][:, O.col_range(4, r, 2)], "b1": p["b1"][O.col_range(4, r, 2)],
+                  "W2": p["W2"][O.col_range(4, r, 2), :], "b2": p["b2"]}
+            part, cache = O.mlp_rank_forward(self.X, pr, r, act="relu", residual=False)
+            np.testing.assert_array_equal(cache["Z"], ts["Y_parts"][r])
+            np.testing.assert_array_equal(part, ts["Z_partials"][r])
+            g = O.mlp_rank_backward(cache, pr, r, dZ, act="relu", residual=False)
+            np.testing.assert_array_equal(dZ @ pr["W2"].T, ts["grad_through_B"][r])
+            np.testing.assert_array_equal((dZ @ pr["W2"].T) * O.relu_grad(cache["U"]), ts["grad_through_relu"][r])
+            np.testing.assert_array_equal(g["dH"], ts["dX_partials"][r])
+            partials.append(part)
+            dx_parts.append(g["dH"])
+        np.testing.assert_array_equal(O.all_reduce_sum(partials), self.g["Z"])
+        np.testing.assert_array_equal(O.all_reduce_sum(dx_parts), self.g["dX"])
+
+    def test_weight_grads_from_printed_intermediates(self):
+        dZ = np.array(self.g["dZ"], float)
+        _, cache = O.mlp_branch_forward(self.X, self.A, 0.0, self.B, 0.0, act="relu")
+        g = O.mlp_branch_backward(cache, self.A, self.B, dZ, act="relu")
+        np.testing.assert_array_equal(g["dW1"], self.g["derived"]["dA"])
+        np.testing.assert_array_equal(g["dW2"], self.g["derived"]["dB"])
+        np.testing.assert_array_equal(g["dH"], self.g["dX"])
+        # the page: dL/dA1 = X^T dL/d(X A1), with GPU 1's gradient through ReLU [1, 1]
+        through_relu_1 = np.array(self.g["two_shards"]["grad_through_relu"][0], float)
+        np.testing.assert_array_equal(self.X.T @ through_relu_1, g["dW1"][:, 0:2])
+
+    @pytest.mark.parametrize("t", [1, 2, 4])
+    def test_4x2_batch_four_shards(self, t):
+        # interview book section 1: X in R^{4x2}, A 2x4, B 4x2, shard i = column i of A, row i of B.
+        # Row 0 is the blog's token; rows 1..3 are seeded (ours).
+        rng = np.random.default_rng(7)
+        X = np.vstack([self.X, rng.standard_normal((3, 2))])
+        dZ = np.vstack([np.ones((1, 2)), rng.standard_normal((3, 2))])
+        partials, dx_parts, dA_cols, dB_rows = [], [], [], []
+        for r in range(t):
+            c = O.col_range(4, r, t)
+            pr = {"W1": self.A[:, c], "b1": np.zeros(4 // t), "W2": self.B[c, :], "b2": np.zeros(2)}
+            part, cache = O.mlp_rank_forward(X, pr, r, act="relu", residual=False)
+            g = O.mlp_rank_backward(cache, pr, r, dZ, act="relu", residual=False)
+            partials.append(part)
+            dx_parts.append(g["dH"])
+            dA_cols.append(g["dW1"])
+            dB_rows.append(g["dW2"])
+            if t == 4:
+                np.testing.assert_array_equal(part[0:1], self.g["derived"]["four_shards_Z_partials"][r])
+                np.testing.assert_array_equal(g["dH"][0:1], self.g["derived"]["four_shards_dX_partials"][r])
+        Z = O.all_reduce_sum(partials)
+        dX = O.all_reduce_sum(dx_parts)
+        np.testing.assert_array_equal(Z[0:1], self.g["Z"])
+        np.testing.assert_array_equal(dX[0:1], self.g["dX"])
+        ref, cache = O.mlp_branch_forward(X, self.A, 0.0, self.B, 0.0, act="relu")
+        gref = O.mlp_branch_backward(cache, self.A, self.B, dZ, act="relu")
+        np.testing.assert_allclose(Z, ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dX, gref["dH"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(np.concatenate(dA_cols, axis=1), gref["dW1"], atol=1e-12)
+        np.testing.assert_allclose(np.concatenate(dB_rows, axis=0), gref["dW2"], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# element-wise closed forms
+# ---------------------------------------------------------------------------
+
+class TestElementwise:
+    g = _golden("softmax_and_collectives.json")
+
+    def test_gelu_against_normal_table(self):
+        x = np.array(self.g["normal_cdf"]["x"])
+        np.testing.assert_allclose(O.gelu(x), x * np.array(self.g["normal_cdf"]["Phi"]), rtol=1e-14)
+
+    def test_gelu_closed_forms(self):
+        x = np.linspace(-6, 6, 97)
+        # Phi(x) + Phi(-x) = 1  =>  GELU(x) - GELU(-x) = x
+        np.testing.assert_allclose(O.gelu(x) - O.gelu(-x), x, atol=1e-14)
+        assert O.gelu(0.0) == 0.0
+        assert O.gelu_grad(0.0) == 0.5
+        np.testing.assert_allclose(O.gelu(np.array([40.0, -40.0])), [40.0, 0.0], atol=1e-300)
+
+    def test_gelu_grad_finite_difference(self):
+        x = np.linspace(-5, 5, 41)
+        eps = 1e-6
+        fd = (O.gelu(x + eps) - O.gelu(x - eps)) / (2 * eps)
+        np.testing.assert_allclose(O.gelu_grad(x), fd, atol=1e-9)
+
+    def test_relu_grad_at_zero(self):
+        # the blog's backward: input [1, 0] passes the gradient [2, 0]
+        np.testing.assert_array_equal(O.relu_grad(np.array([1.0, 0.0])), [1.0, 0.0])
+
+    def test_softmax_page_values(self):
+        os_ = self.g["online_softmax"]
+        w = O.softmax_rows(np.array([os_["scores"]], float))[0]
+        np.testing.assert_allclose(np.round(w, 3), os_["weights"], atol=0)
+        assert round(math.exp(os_["scores"][0] - os_["scores"][1]), 3) == os_["rescale_factor"]
+
+    def test_softmax_properties(self):
+        rng = np.random.default_rng(3)
+        S = rng.standard_normal((5, 9)) * 4
+        P = O.softmax_rows(S)
+        np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-15)
+        np.testing.assert_allclose(O.softmax_rows(S + 123.0), P, atol=1e-15)
+        S[:, 5:] = -np.inf
+        P = O.softmax_rows(S)
+        assert np.all(P[:, 5:] == 0.0)
+
+    def test_all_reduce_page_example(self):
+        ar = self.g["all_reduce"]
+        np.testing.assert_array_equal(O.all_reduce_sum([np.array(v, float) for v in ar["inputs"]]), ar["output"])
+
+    def test_causal_visibility_table(self):
+        cv = self.g["causal_visibility"]
+        np.testing.assert_array_equal(~O.causal_mask(cv["tokens"]), np.array(cv["visible"], bool))
+
+
+# ---------------------------------------------------------------------------
+# attention: brute force and special cases
+# ---------------------------------------------------------------------------
+
+def _brute_attention(Q, K, V, s, b, heads):
+    """Pure-Python loops over the definition: for each sequence, head and
+    query, softmax over the visible keys, then the weighted sum of values."""
+    d = Q.shape[1] // heads
+    C = np.zeros_like(Q)
+    for beta in range(b):
+        for j in range(heads):
+            cols = range(j * d, (j + 1) * d)
+            for i in range(s):
+                qi = i * b + beta
+                logits = []
+                for k in range(i + 1):
+                    kk = k * b + beta
+                    logits.append(sum(Q[qi, c] * K[kk, c] for c in cols) / math.sqrt(d))
+                mx = max(logits)
+                w = [math.exp(x - mx) for x in logits]
+                tot = sum(w)
+                for c in cols:
+                    C[qi, c] = sum(w[k] * V[k * b + beta, c] for k in range(i + 1)) / tot
+    return C
+
+
+def test_attention_matches_brute_force():
+    rng = np.random.default_rng(11)
+    s, b, heads, d = 5, 2, 3, 4
+    Q, K, V = (rng.standard_normal((s * b, heads * d)) for _ in range(3))
+    C, P = O.attention_core_forward(Q, K, V, s, b, heads)
+    np.testing.assert_allclose(C, _brute_attention(Q, K, V, s, b, heads), atol=1e-13)
+    assert np.all(np.triu(P, k=1) == 0.0)
+
+
+def test_first_query_sees_only_itself():
+    rng = np.random.default_rng(12)
+    s, b, heads = 6, 3, 2
+    Q, K, V = (rng.standard_normal((s * b, heads * 5)) for _ in range(3))
+    C, _ = O.attention_core_forward(Q, K, V, s, b, heads)
+    np.testing.assert_allclose(C[:b], V[:b], atol=1e-15)
+
+
+def test_zero_queries_give_prefix_mean():
+    rng = np.random.default_rng(13)
+    s, b, heads = 7, 2, 2
+    K, V = (rng.standard_normal((s * b, heads * 3)) for _ in range(2))
+    Q = np.zeros_like(K)
+    C, _ = O.attention_core_forward(Q, K, V, s, b, heads)
+    for beta in range(b):
+        rows = V[beta::b]
+        prefix_mean = np.cumsum(rows, axis=0) / np.arange(1, s + 1)[:, None]
+        np.testing.assert_allclose(C[beta::b], prefix_mean, atol=1e-14)
+
+
+def test_layer_is_causal_and_sequences_independent():
+    rng = np.random.default_rng(14)
+    h, a, s, b = 16, 2, 6, 2
+    p = _rand_params(rng, h, 4 * h)
+    X = rng.standard_normal((s * b, h))
+    Y, _ = O.layer_forward(X, p, s, b, a)
+    k = 3
+    X2 = X.copy()
+    X2[k * b + 1] += 5.0  # token k of sequence 1
+    Y2, _ = O.layer_forward(X2, p, s, b, a)
+    np.testing.assert_array_equal(Y2[: k * b], Y[: k * b])         # earlier tokens unchanged
+    np.testing.assert_array_equal(Y2[0::b], Y[0::b])                # other sequence unchanged
+    assert np.abs(Y2[k * b + 1] - Y[k * b + 1]).max() > 1e-3
+
+
+def test_block_residual_structure():
+    rng = np.random.default_rng(15)
+    h, a, s, b = 16, 4, 4, 2
+    p = _rand_params(rng, h, 4 * h)
+    X = rng.standard_normal((s * b, h))
+    p0 = dict(p, Wo=np.zeros((h, h)), bo=np.zeros(h))
+    H, _ = O.attention_block_forward(X, p0, s, b, a)
+    np.testing.assert_array_equal(H, X)
+    p1 = dict(p, W2=np.zeros((4 * h, h)), b2=np.zeros(h))
+    Y, _ = O.mlp_block_forward(X, p1)
+    np.testing.assert_array_equal(Y, X)
+
+
+# ---------------------------------------------------------------------------
+# tensor-parallel invariant: the sum over ranks equals the unsharded layer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_sharded_equals_unsharded(t):
+    rng = np.random.default_rng(20 + t)
+    h, a, s, b = 32, 8, 8, 2
+    p = _rand_params(rng, h, 4 * h, std=0.2)
+    X = rng.standard_normal((s * b, h))
+    dY = rng.standard_normal((s * b, h))
+    Y, cache = O.layer_forward(X, p, s, b, a)
+    g = O.layer_backward(cache, p, dY, s, b, a)
+    ar = a // t
+
+    attn_parts, ranks = [], []
+    for r in range(t):
+        pr = O.shard_params(p, r, t)
+        part, ca = O.attention_rank_forward(X, pr, r, s, b, ar)
+        attn_parts.append(part)
+        ranks.append((pr, ca))
+    H = O.all_reduce_sum(attn_parts)
+    np.testing.assert_allclose(H, cache["H"], atol=1e-12)
+
+    mlp_parts, mcaches = [], []
+    for r in range(t):
+        part, cm = O.mlp_rank_forward(H, ranks[r][0], r)
+        mlp_parts.append(part)
+        mcaches.append(cm)
+    np.testing.assert_allclose(O.all_reduce_sum(mlp_parts), Y, atol=1e-12)
+
+    gm = [O.mlp_rank_backward(mcaches[r], ranks[r][0], r, dY) for r in range(t)]
+    dH = O.all_reduce_sum([x["dH"] for x in gm])
+    np.testing.assert_allclose(dH, g["dH"], atol=1e-12)
+    ga = [O.attention_rank_backward(ranks[r][1], ranks[r][0], r, dH, s, b, ar) for r in range(t)]
+    np.testing.assert_allclose(O.all_reduce_sum([x["dX"] for x in ga]), g["dX"], atol=1e-12)
+
+    # shards concatenate to the unsharded gradients; replicas agree everywhere
+    for name, axis in (("dW1", 1), ("db1", 0), ("dW2", 0)):
+        np.testing.assert_allclose(np.concatenate([x[name] for x in gm], axis=axis), g[name], atol=1e-12)
+    for name, axis in (("dWq", 1), ("dWk", 1), ("dWv", 1), ("dbq", 0), ("dbk", 0), ("dbv", 0), ("dWo", 0)):
+        np.testing.assert_allclose(np.concatenate([x[name] for x in ga], axis=axis), g[name], atol=1e-12)
+    for x in gm:
+        np.testing.assert_allclose(x["db2"], g["db2"], atol=1e-12)
+    for x in ga:
+        np.testing.assert_allclose(x["dbo"], g["dbo"], atol=1e-12)
+
+
+def test_t1_rank_is_the_unsharded_block():
+    rng = np.random.default_rng(30)
+    h, a, s, b = 16, 2, 4, 3
+    p = _rand_params(rng, h, 4 * h)
+    X = rng.standard_normal((s * b, h))
+    part, _ = O.attention_rank_forward(X, O.shard_params(p, 0, 1), 0, s, b, a)
+    H, _ = O.attention_block_forward(X, p, s, b, a)
+    np.testing.assert_allclose(part, H, rtol=0, atol=1e-14)  # only the order of the adds differs
+
+
+# ---------------------------------------------------------------------------
+# gradients: central finite differences of L = sum(Y * dY)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(8, 2, 4, 2), (16, 4, 3, 2)])
+def test_gradients_finite_differences(shape):
+    h, a, s, b = shape
+    rng = np.random.default_rng(40 + h)
+    p = _rand_params(rng, h, 4 * h, std=0.4)
+    X = rng.standard_normal((s * b, h))
+    dY = rng.standard_normal((s * b, h))
+    Y, cache = O.layer_forward(X, p, s, b, a)
+    g = O.layer_backward(cache, p, dY, s, b, a)
+
+    def loss(pp, XX):
+        return float(np.sum(O.layer_forward(XX, pp, s, b, a)[0] * dY))
+
+    eps = 1e-5
+    tensors = dict(p, X=X)
+    for name, arr in tensors.items():
+        grad = g["d" + name]
+        flat_idx = rng.choice(arr.size, size=min(arr.size, 6), replace=False)
+        for fi in flat_idx:
+            idx = np.unravel_index(fi, arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            if name == "X":
+                fd = (loss(p, plus) - loss(p, minus)) / (2 * eps)
+            else:
+                fd = (loss(dict(p, **{name: plus}), X) - loss(dict(p, **{name: minus}), X)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+# ---------------------------------------------------------------------------
+# FLOP accounting: Eq. 3 per rank equals the sum over the layer's products
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(I.CONFIGS))
+def test_flops_formula_equals_gemm_count(name):
+    c = I.CONFIGS[name]
+    h, s, b, t = c.h, c.s, c.b, c.t
+    T = s * b
+    lin = [(T, 3 * h // t, h), (T, h, h // t), (T, 4 * h // t, h), (T, h, 4 * h // t)]
+    fwd = sum(2 * m * n * k for m, n, k in lin)
+    # scores and context, full s^2 per (sequence, head) as Eq. 3 counts them
+    fwd += 2 * (2 * b * (c.a // t) * s * s * c.d)
+    assert 3 * fwd == pytest.approx(O.model_flops_per_rank(h, s, b, t), rel=1e-12)
