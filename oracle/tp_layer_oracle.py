@@ -42,8 +42,9 @@ Readings where the pages are silent (each is listed in the design notes):
 GELU is the exact erf form; biases exist on all four linears; the causal
 mask lets query i see keys k <= i; the softmax scale is 1/sqrt(d_head); the
 QKV shard of rank r is the contiguous column range c_r of each of Wq, Wk, Wv;
-replicated terms (output biases and residuals) are folded into rank 0's
-partial, which leaves the sum over ranks unchanged.
+replicated terms (the output bias and the residual) are added once, after
+the all-reduce of the partials, as the fused bias+dropout+add of the
+paper-graph page's "Computation Optimizations" (here without dropout).
 
 Parity pins live in tests/test_oracle_pins.py: the blog's worked MLP values,
 closed forms of GELU and the softmax, brute-force loops on tiny inputs,
@@ -269,29 +270,28 @@ def shard_params(p, r, t):
     }
 
 
-def attention_rank_forward(X, pr, rank, s, b, heads_r):
-    """Rank `rank`'s partial of the attention block.
+def attention_rank_forward(X, pr, s, b, heads_r):
+    """Rank's partial of the attention block: C_r Wo_r.
 
     The rank projects X (replicated: f is the identity forward) onto its own
     heads, runs their attention locally, and multiplies by its rows of Wo.
-    The replicated bias bo and the residual X are added by rank 0 only.
+    The output bias and the residual are not part of any rank's partial: they
+    are added after the all-reduce (see block_output).
     """
     X = np.asarray(X, dtype=F64)
     Q = X @ pr["Wq"] + pr["bq"]
     K = X @ pr["Wk"] + pr["bk"]
     V = X @ pr["Wv"] + pr["bv"]
     C, P = attention_core_forward(Q, K, V, s, b, heads_r)
-    part = C @ pr["Wo"]
-    if rank == 0:
-        part = part + pr["bo"] + X
-    return part, dict(X=X, Q=Q, K=K, V=V, P=P, C=C)
+    return C @ pr["Wo"], dict(X=X, Q=Q, K=K, V=V, P=P, C=C)
 
 
-def attention_rank_backward(cache, pr, rank, dH, s, b, heads_r):
+def attention_rank_backward(cache, pr, dH, s, b, heads_r):
     """Rank-local backward of the attention block given the replicated dH
-    (g's backward is the identity).  Returns the rank's partial dX (summed
-    over ranks by f's backward all-reduce; rank 0 adds the residual path),
-    its weight/bias gradient shards, and dbo (a replica)."""
+    (g's backward is the identity).  Returns the rank's partial of dL/dX
+    through its own heads (summed over ranks by f's backward all-reduce; the
+    residual path dH is added once after it, see block_output), its weight and
+    bias gradient shards, and dbo (a replica, equal on every rank)."""
     dH = np.asarray(dH, dtype=F64)
     X, C = cache["X"], cache["C"]
     g = {"dWo": C.T @ dH, "dbo": dH.sum(axis=0)}
@@ -299,29 +299,34 @@ def attention_rank_backward(cache, pr, rank, dH, s, b, heads_r):
     dQ, dK, dV = attention_core_backward(cache["Q"], cache["K"], cache["V"], cache["P"], dC, s, b, heads_r)
     g.update(dWq=X.T @ dQ, dWk=X.T @ dK, dWv=X.T @ dV,
              dbq=dQ.sum(axis=0), dbk=dK.sum(axis=0), dbv=dV.sum(axis=0))
-    dX = dQ @ pr["Wq"].T + dK @ pr["Wk"].T + dV @ pr["Wv"].T
-    if rank == 0:
-        dX = dX + dH
-    g["dX"] = dX
+    g["dX"] = dQ @ pr["Wq"].T + dK @ pr["Wk"].T + dV @ pr["Wv"].T
     g["dC"] = dC
     return g
 
 
-def mlp_rank_forward(H, pr, rank, act="gelu", residual=True):
-    """Rank's partial act(H W1_r + b1_r) W2_r (+ b2 + H on rank 0)."""
-    out, cache = mlp_branch_forward(H, pr["W1"], pr["b1"], pr["W2"], 0.0, act)
-    if rank == 0:
-        out = out + pr["b2"]
-        if residual:
-            out = out + cache["H"]
-    return out, cache
+def mlp_rank_forward(H, pr, act="gelu"):
+    """Rank's partial act(H W1_r + b1_r) W2_r; b2 and the residual are added
+    after the all-reduce."""
+    return mlp_branch_forward(H, pr["W1"], pr["b1"], pr["W2"], 0.0, act)
 
 
-def mlp_rank_backward(cache, pr, rank, dY, act="gelu", residual=True):
-    g = mlp_branch_backward(cache, pr["W1"], pr["W2"], dY, act)
-    if rank == 0 and residual:
-        g["dH"] = g["dH"] + np.asarray(dY, dtype=F64)
-    return g
+def mlp_rank_backward(cache, pr, dY, act="gelu"):
+    """Rank's partial of dL/dH through its FC1/FC2 shards (the residual path
+    dY is added after the all-reduce), its W1/b1/W2 shards' gradients and db2
+    (a replica)."""
+    return mlp_branch_backward(cache, pr["W1"], pr["W2"], dY, act)
+
+
+def block_output(partials, bias=None, residual=None):
+    """After the all-reduce: residual + bias + sum of the ranks' partials (the
+    fused bias + dropout + residual add, without dropout).  In the backward the
+    same routine adds the residual gradient to the summed partials."""
+    out = all_reduce_sum(partials)
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=F64)
+    if residual is not None:
+        out = out + np.asarray(residual, dtype=F64)
+    return out
 
 
 # ---------------------------------------------------------------------------

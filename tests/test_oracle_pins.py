@@ -57,10 +57,10 @@ class TestWorkedExample:
         for r in range(2):
             pr = {"W1": p["W1"][:, O.col_range(4, r, 2)], "b1": p["b1"][O.col_range(4, r, 2)],
                   "W2": p["W2"][O.col_range(4, r, 2), :], "b2": p["b2"]}
-            part, cache = O.mlp_rank_forward(self.X, pr, r, act="relu", residual=False)
+            part, cache = O.mlp_rank_forward(self.X, pr, act="relu")
             np.testing.assert_array_equal(cache["Z"], ts["Y_parts"][r])
             np.testing.assert_array_equal(part, ts["Z_partials"][r])
-            g = O.mlp_rank_backward(cache, pr, r, dZ, act="relu", residual=False)
+            g = O.mlp_rank_backward(cache, pr, dZ, act="relu")
             np.testing.assert_array_equal(dZ @ pr["W2"].T, ts["grad_through_B"][r])
             np.testing.assert_array_equal((dZ @ pr["W2"].T) * O.relu_grad(cache["U"]), ts["grad_through_relu"][r])
             np.testing.assert_array_equal(g["dH"], ts["dX_partials"][r])
@@ -91,8 +91,8 @@ class TestWorkedExample:
         for r in range(t):
             c = O.col_range(4, r, t)
             pr = {"W1": self.A[:, c], "b1": np.zeros(4 // t), "W2": self.B[c, :], "b2": np.zeros(2)}
-            part, cache = O.mlp_rank_forward(X, pr, r, act="relu", residual=False)
-            g = O.mlp_rank_backward(cache, pr, r, dZ, act="relu", residual=False)
+            part, cache = O.mlp_rank_forward(X, pr, act="relu")
+            g = O.mlp_rank_backward(cache, pr, dZ, act="relu")
             partials.append(part)
             dx_parts.append(g["dH"])
             dA_cols.append(g["dW1"])
@@ -267,24 +267,25 @@ def test_sharded_equals_unsharded(t):
     attn_parts, ranks = [], []
     for r in range(t):
         pr = O.shard_params(p, r, t)
-        part, ca = O.attention_rank_forward(X, pr, r, s, b, ar)
+        part, ca = O.attention_rank_forward(X, pr, s, b, ar)
         attn_parts.append(part)
         ranks.append((pr, ca))
-    H = O.all_reduce_sum(attn_parts)
+    # all-reduce, then the fused bias + residual add
+    H = O.block_output(attn_parts, p["bo"], X)
     np.testing.assert_allclose(H, cache["H"], atol=1e-12)
 
     mlp_parts, mcaches = [], []
     for r in range(t):
-        part, cm = O.mlp_rank_forward(H, ranks[r][0], r)
+        part, cm = O.mlp_rank_forward(H, ranks[r][0])
         mlp_parts.append(part)
         mcaches.append(cm)
-    np.testing.assert_allclose(O.all_reduce_sum(mlp_parts), Y, atol=1e-12)
+    np.testing.assert_allclose(O.block_output(mlp_parts, p["b2"], H), Y, atol=1e-12)
 
-    gm = [O.mlp_rank_backward(mcaches[r], ranks[r][0], r, dY) for r in range(t)]
-    dH = O.all_reduce_sum([x["dH"] for x in gm])
+    gm = [O.mlp_rank_backward(mcaches[r], ranks[r][0], dY) for r in range(t)]
+    dH = O.block_output([x["dH"] for x in gm], residual=dY)
     np.testing.assert_allclose(dH, g["dH"], atol=1e-12)
-    ga = [O.attention_rank_backward(ranks[r][1], ranks[r][0], r, dH, s, b, ar) for r in range(t)]
-    np.testing.assert_allclose(O.all_reduce_sum([x["dX"] for x in ga]), g["dX"], atol=1e-12)
+    ga = [O.attention_rank_backward(ranks[r][1], ranks[r][0], dH, s, b, ar) for r in range(t)]
+    np.testing.assert_allclose(O.block_output([x["dX"] for x in ga], residual=dH), g["dX"], atol=1e-12)
 
     # shards concatenate to the unsharded gradients; replicas agree everywhere
     for name, axis in (("dW1", 1), ("db1", 0), ("dW2", 0)):
@@ -302,9 +303,9 @@ def test_t1_rank_is_the_unsharded_block():
     h, a, s, b = 16, 2, 4, 3
     p = _rand_params(rng, h, 4 * h)
     X = rng.standard_normal((s * b, h))
-    part, _ = O.attention_rank_forward(X, O.shard_params(p, 0, 1), 0, s, b, a)
+    part, _ = O.attention_rank_forward(X, O.shard_params(p, 0, 1), s, b, a)
     H, _ = O.attention_block_forward(X, p, s, b, a)
-    np.testing.assert_allclose(part, H, rtol=0, atol=1e-14)  # only the order of the adds differs
+    np.testing.assert_allclose(O.block_output([part], p["bo"], X), H, rtol=0, atol=1e-14)
 
 
 # ---------------------------------------------------------------------------
