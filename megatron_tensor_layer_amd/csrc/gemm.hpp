@@ -1,0 +1,404 @@
+// MFMA GEMM for gfx950: C = epilogue(op(A) * op(B)), bf16 or fp32 operands,
+// fp32 accumulation, LDS-staged double-buffered tiles, fused epilogues.
+//
+// Design (CDNA4, 64-wide waves):
+//  * A block computes a BM x BN tile with WM x WN waves; each wave owns a
+//    (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles
+//    (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2_f32 for fp32).
+//  * Both operands are staged in LDS "K-contiguous": one 128-byte LDS row
+//    holds BK = 64 bf16 (32 fp32) consecutive k of one m (or n) index, so an
+//    MFMA fragment (8 bf16 / 4 fp32 consecutive k of one row) is a single
+//    16-byte LDS read. The eight 16-byte chunks of a row are XOR-swizzled by
+//    (row & 7), which makes both the fragment reads and the stores
+//    bank-conflict free.
+//  * An operand stored K-contiguous in HBM (e.g. X in X W, or W in dY W^T) is
+//    copied chunk by chunk. An operand stored M/N-contiguous (W in X W, both
+//    operands of a weight gradient X^T dY) is read as VECxVEC element blocks
+//    (VEC rows of k, 16 bytes along m/n each) and transposed in registers
+//    before the LDS store, so the LDS layout and the inner loop are the same
+//    for every operand orientation.
+//  * fp32 MFMA pairs lanes 0-31 / 32-63 with k = 0 / 1 of each 32x32x2 step;
+//    feeding element e of a 4-float chunk to step e makes one 16-byte
+//    fragment cover 8 k values in 4 steps. A and B use the same k order, so
+//    the sum over k is unchanged.
+//  * The MFMA is issued with the B fragment as its first operand, which puts
+//    one output row m and four consecutive columns n in each lane: epilogues
+//    load bias / residual / aux values and store results 4 elements at a time.
+//  * Tiles are ordered in groups of GM tile-rows and remapped so that
+//    consecutive tiles land on the same XCD (workgroups are dealt to the 8
+//    XCDs round-robin), so co-resident blocks share A and B panels in L2.
+//  * Causal (lower-triangular) tile sets and causal K ranges serve the
+//    attention products; split-K writes fp32 partials reduced in a fixed
+//    order by a second kernel (no atomics, deterministic).
+#pragma once
+
+#include "tp_common.hpp"
+
+namespace tpl {
+
+enum EpiKind : int {
+  EPI_LINEAR = 0,       // C = alpha*acc (+ bias[n]) (+ resid[m,n])
+  EPI_BIAS_GELU = 1,    // U = acc + bias[n] -> C;  GELU(U) -> C2
+  EPI_GELU_BWD = 2,     // C = acc * gelu'(aux[m,n])
+  EPI_SOFTMAX_BWD = 3,  // C = (n <= m) ? alpha * aux[m,n] * (acc - rowv[m]) : 0
+  EPI_PARTIAL = 4       // split-K: fp32 partial[split, m, n] = acc
+};
+
+enum KMode : int {
+  K_FULL = 0,   // k in [0, K)
+  K_LOWER = 1,  // k in [0, min(K, m0 + BM))   (causal: key <= query)
+  K_UPPER = 2   // k in [m0, K)                 (causal: query >= key)
+};
+
+struct GemmArgs {
+  int M, N, K;
+  int zdiv;              // batch z -> (z1, z2) = (z / zdiv, z % zdiv)
+  int tiles_m, tiles_n;  // set by the launcher
+  int tri;               // 1: only tiles with tile_n <= tile_m (BM == BN)
+  int kmode;
+  int splits, k_chunk;   // split-K (EPI_PARTIAL pass)
+  int group_m;           // tile-rows per ordering group
+  const void* A; long lda, a_s1, a_s2;
+  const void* B; long ldb, b_s1, b_s2;
+  void* C; long ldc, c_s1, c_s2;
+  void* C2; long ldc2;
+  const void* bias;
+  const void* resid; long ldr;
+  const void* aux; long ldx, x_s1, x_s2;
+  const float* rowv; long r_s1, r_s2;
+  float alpha;
+  float* part;
+};
+
+template <typename T_, int BM_, int BN_, int WM_, int WN_>
+struct TileCfg {
+  using T = T_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int BK = 8 * VEC;  // one 128-byte LDS row
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static constexpr int LDS_BYTES = 2 * (BM + BN) * 128;
+};
+
+// ---------------------------------------------------------------------------
+// global -> LDS loaders
+// ---------------------------------------------------------------------------
+
+// Operand stored K-contiguous: element (row, k) at base[row*ld + k].
+template <typename T, int R, int NT>
+struct KLoader {
+  static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int TOTAL = R * 8;  // 16-byte chunks in an R x BK tile
+  static constexpr int CH = (TOTAL + NT - 1) / NT;
+  uint4 v[CH];
+
+  __device__ __forceinline__ void load(const T* base, long ld, int row0, int rlim, int k0, int ke, int tid) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * NT;
+      const int r = c >> 3, kc = c & 7;
+      const int row = row0 + r, k = k0 + kc * VEC;
+      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && row < rlim && k < ke;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) x = *reinterpret_cast<const uint4*>(base + (long)row * ld + k);
+      v[i] = x;
+    }
+  }
+  __device__ __forceinline__ void store(uint4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * NT;
+      if (TOTAL % NT == 0 || c < TOTAL) {
+        const int r = c >> 3, kc = c & 7;
+        lds[r * 8 + (kc ^ (r & 7))] = v[i];
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t dw(const uint4& x, int q) {
+  return q == 0 ? x.x : (q == 1 ? x.y : (q == 2 ? x.z : x.w));
+}
+
+// in[r] = 8 bf16 (k = r, mn = 0..7)  ->  out[j] = 8 bf16 (k = 0..7, mn = j)
+__device__ __forceinline__ void transpose_blk(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = dw(in[2 * q], j >> 1), hi = dw(in[2 * q + 1], j >> 1);
+      w[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    out[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// in[r] = 4 fp32 (k = r, mn = 0..3)  ->  out[j] = 4 fp32 (k = 0..3, mn = j)
+__device__ __forceinline__ void transpose_blk(const uint4 (&in)[4], uint4 (&out)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = make_uint4(dw(in[0], j), dw(in[1], j), dw(in[2], j), dw(in[3], j));
+}
+
+// Operand stored M/N-contiguous: element (mn, k) at base[k*ld + mn].
+template <typename T, int R, int NT>
+struct MNLoader {
+  static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int TOTAL = (R / VEC) * 8;  // VEC x VEC blocks in an R x BK tile
+  static constexpr int BPT = (TOTAL + NT - 1) / NT;
+  uint4 v[BPT][VEC];
+
+  __device__ __forceinline__ void load(const T* base, long ld, int mn0, int mnlim, int k0, int ke, int tid) {
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      const int c = tid + b * NT;
+      const int kc = c & 7, mb = c >> 3;
+      const int mn = mn0 + mb * VEC;
+      const bool okb = (TOTAL % NT == 0 || c < TOTAL) && mn < mnlim;
+#pragma unroll
+      for (int r = 0; r < VEC; ++r) {
+        const int k = k0 + kc * VEC + r;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (okb && k < ke) x = *reinterpret_cast<const uint4*>(base + (long)k * ld + mn);
+        v[b][r] = x;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint4* lds, int tid) const {
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      const int c = tid + b * NT;
+      if (TOTAL % NT == 0 || c < TOTAL) {
+        const int kc = c & 7, mb = c >> 3;
+        uint4 w[VEC];
+        transpose_blk(v[b], w);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          const int row = mb * VEC + j;
+          lds[row * 8 + (kc ^ (row & 7))] = w[j];
+        }
+      }
+    }
+  }
+};
+
+template <bool KMAJ, typename T, int R, int NT>
+struct LoaderSel {
+  using type = KLoader<T, R, NT>;
+};
+template <typename T, int R, int NT>
+struct LoaderSel<false, T, R, NT> {
+  using type = MNLoader<T, R, NT>;
+};
+
+// ---------------------------------------------------------------------------
+// MFMA step on one 16-byte fragment pair
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void mma16(const uint4& bfrag, const uint4& afrag, f32x16_t& acc, bf16_t) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bfrag),
+                                                __builtin_bit_cast(bf16x8_t, afrag), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(const uint4& bfrag, const uint4& afrag, f32x16_t& acc, float) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(bfrag.x), __uint_as_float(afrag.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(bfrag.y), __uint_as_float(afrag.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(bfrag.z), __uint_as_float(afrag.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(bfrag.w), __uint_as_float(afrag.w), acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// epilogue on 4 consecutive columns of one row
+// ---------------------------------------------------------------------------
+
+template <int EPI, typename T, typename TO>
+__device__ __forceinline__ void epi_apply(const GemmArgs& p, int z1, int z2, int row, int col, float v[4], int split) {
+  if constexpr (EPI == EPI_PARTIAL) {
+    Elt<float>::store4(p.part + ((long)split * p.M + row) * (long)p.N + col, v);
+    return;
+  } else {
+    if constexpr (EPI == EPI_LINEAR) {
+      if (p.alpha != 1.0f) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= p.alpha;
+      }
+      if (p.bias) {
+        float bb[4];
+        Elt<T>::load4(static_cast<const T*>(p.bias) + col, bb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += bb[e];
+      }
+      if (p.resid) {
+        float rr[4];
+        Elt<T>::load4(static_cast<const T*>(p.resid) + (long)row * p.ldr + col, rr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += rr[e];
+      }
+    } else if constexpr (EPI == EPI_BIAS_GELU) {
+      float bb[4];
+      Elt<T>::load4(static_cast<const T*>(p.bias) + col, bb);
+      float g[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] += bb[e];
+        g[e] = gelu_f(v[e]);
+      }
+      Elt<T>::store4(static_cast<T*>(p.C2) + (long)row * p.ldc2 + col, g);
+    } else if constexpr (EPI == EPI_GELU_BWD) {
+      float u[4];
+      Elt<T>::load4(static_cast<const T*>(p.aux) + (long)row * p.ldx + col, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+    } else if constexpr (EPI == EPI_SOFTMAX_BWD) {
+      float pp[4];
+      Elt<T>::load4(static_cast<const T*>(p.aux) + z1 * p.x_s1 + z2 * p.x_s2 + (long)row * p.ldx + col, pp);
+      const float D = p.rowv[z1 * p.r_s1 + z2 * p.r_s2 + row];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (col + e <= row) ? p.alpha * pp[e] * (v[e] - D) : 0.0f;
+    }
+    Elt<TO>::store4(static_cast<TO*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tile scheduling
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
+  int L = blockIdx.x;
+  if (p.tri) {
+    int m = (int)((sqrtf(8.0f * (float)L + 1.0f) - 1.0f) * 0.5f);
+    while ((m + 1) * (m + 2) / 2 <= L) ++m;
+    while (m * (m + 1) / 2 > L) --m;
+    tm = m;
+    tn = L - m * (m + 1) / 2;
+    return;
+  }
+  const int tiles = p.tiles_m * p.tiles_n;
+  if ((tiles & 7) == 0) L = (L & 7) * (tiles >> 3) + (L >> 3);  // same-XCD runs of tiles
+  const int per_group = p.group_m * p.tiles_n;
+  const int grp = L / per_group, first = grp * p.group_m;
+  const int gs = min(p.tiles_m - first, p.group_m);
+  const int w = L - grp * per_group;
+  tm = first + w % gs;
+  tn = w / gs;
+  if (p.kmode == K_LOWER) tm = p.tiles_m - 1 - tm;  // longest K ranges first
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+
+// ROLE only names the instantiation (one kernel symbol per GEMM of the layer,
+// so profilers attribute time per GEMM); it does not change the code.
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE>
+__global__ void __launch_bounds__(Cfg::NT) gemm_kernel(const GemmArgs p) {
+  using T = typename Cfg::T;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BK = Cfg::BK;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;
+  __shared__ uint4 smem[2 * (BM + BN) * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WN, wn = wave - (wave / Cfg::WN) * Cfg::WN;
+
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.z, z1 = z / p.zdiv, z2 = z - (z / p.zdiv) * p.zdiv;
+  const T* A = static_cast<const T*>(p.A) + z1 * p.a_s1 + z2 * p.a_s2;
+  const T* B = static_cast<const T*>(p.B) + z1 * p.b_s1 + z2 * p.b_s2;
+
+  int kb = 0, ke = p.K;
+  if (p.kmode == K_LOWER) ke = min(ke, m0 + BM);
+  else if (p.kmode == K_UPPER) kb = m0;
+  if constexpr (EPI == EPI_PARTIAL) {
+    kb = blockIdx.y * p.k_chunk;
+    ke = min(ke, kb + p.k_chunk);
+  }
+  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  typename LoaderSel<AK, T, BM, NT>::type la;
+  typename LoaderSel<BKM, T, BN, NT>::type lb;
+
+  if (nk > 0) {
+    la.load(A, p.lda, m0, p.M, kb, ke, tid);
+    lb.load(B, p.ldb, n0, p.N, kb, ke, tid);
+    la.store(smem, tid);
+    lb.store(smem + BM * 8, tid);
+  }
+  __syncthreads();
+
+  const int r32 = lane & 31, g = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint4* As = smem + (kt & 1) * (BM + BN) * 8;
+    const uint4* Bs = As + BM * 8;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int kn = kb + (kt + 1) * BK;
+      la.load(A, p.lda, m0, p.M, kn, ke, tid);
+      lb.load(B, p.ldb, n0, p.N, kn, ke, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = (2 * ks + g) ^ (r32 & 7);
+      uint4 af[TM], bq[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = As[(wm * WTM + i * 32 + r32) * 8 + ch];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bq[j] = Bs[(wn * WTN + j * 32 + r32) * 8 + ch];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) mma16(bq[j], af[i], acc[i][j], T{});
+    }
+    if (more) {
+      uint4* An = smem + ((kt + 1) & 1) * (BM + BN) * 8;
+      la.store(An, tid);
+      lb.store(An + BM * 8, tid);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm * WTM + i * 32 + r32;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = n0 + wn * WTN + j * 32 + jj * 8 + g * 4;
+        float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
+        if (row < p.M && col < p.N) epi_apply<EPI, T, TO>(p, z1, z2, row, col, v, blockIdx.y);
+      }
+    }
+  }
+}
+
+// Fixed-order sum of split-K partials followed by the real epilogue (batch 1).
+template <int EPI, typename T, typename TO, int ROLE>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
+  const long n4 = p.N / 4;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)p.M * n4) return;
+  const int row = (int)(idx / n4), col = (int)(idx - (idx / n4) * n4) * 4;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.splits; ++s) {
+    float x[4];
+    Elt<float>::load4(p.part + ((long)s * p.M + row) * (long)p.N + col, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += x[e];
+  }
+  epi_apply<EPI, T, TO>(p, 0, 0, row, col, v, 0);
+}
+
+}  // namespace tpl

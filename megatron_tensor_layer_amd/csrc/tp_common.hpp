@@ -1,0 +1,68 @@
+// Common types and device helpers for the gfx950 kernels of libtplayer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpl {
+
+typedef uint16_t bf16_t;  // bfloat16 storage (upper half of an fp32)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// round-to-nearest-even through the hardware converter (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+// Element traits: load / store 4 consecutive elements as fp32.
+template <typename T> struct Elt;
+
+template <> struct Elt<float> {
+  static constexpr int VEC = 4;  // elements per 16-byte chunk
+  __device__ static __forceinline__ void load4(const float* p, float v[4]) {
+    f32x4_t x = *reinterpret_cast<const f32x4_t*>(p);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  }
+  __device__ static __forceinline__ void store4(float* p, const float v[4]) {
+    f32x4_t x = {v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4_t*>(p) = x;
+  }
+  __device__ static __forceinline__ float ld(const float* p) { return *p; }
+  __device__ static __forceinline__ void st(float* p, float v) { *p = v; }
+};
+
+template <> struct Elt<bf16_t> {
+  static constexpr int VEC = 8;
+  __device__ static __forceinline__ void load4(const bf16_t* p, float v[4]) {
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  }
+  __device__ static __forceinline__ void store4(bf16_t* p, const float v[4]) {
+    f32x4_t x = {v[0], v[1], v[2], v[3]};
+    bf16x4_t b = __builtin_convertvector(x, bf16x4_t);
+    *reinterpret_cast<bf16x4_t*>(p) = b;
+  }
+  __device__ static __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  __device__ static __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Exact (erf-form) GELU and its derivative in fp32.
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad_f(float x) {
+  const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
+  const float pdf = 0.39894228040143268f * expf(-0.5f * x * x);
+  return cdf + x * pdf;
+}
+
+__host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr inline long cdivl(long a, long b) { return (a + b - 1) / b; }
+
+}  // namespace tpl

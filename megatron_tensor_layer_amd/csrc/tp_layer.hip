@@ -1,0 +1,741 @@
+// libtplayer: C ABI for one tensor-parallel rank's share of a GPT layer on
+// gfx950. Host code validates arguments, lays out the saved activations and
+// the workspace, and enqueues the kernels of gemm.hpp / aux_kernels.hpp on
+// the caller's stream. The library allocates no device memory; its only
+// state is the calling thread's last HIP error text and, while profiling is
+// switched on, the HIP events of the profiled launches.
+//
+// Block flows (rank r; paper-graph page, section 3 "Tensor Model
+// Parallelism: The Megatron Partitioning"; "parallelism" blog, "Tensor
+// parallelism: split every matrix" and "The backward pass"):
+//   ATTN fwd:  QKV = X Wqkv_r + b (GEMM, bias epilogue)
+//              S = Q K^T / sqrt(d) per (sequence, head), causal tiles only
+//              P = causal softmax(S);  C = P V (causal K range)
+//              partial = C Wo_r
+//   MLP fwd:   U = H W1_r + b1, Z = GELU(U) (one GEMM, dual-store epilogue)
+//              partial = Z W2_r
+//   MLP bwd:   dU = (dY W2_r^T) * GELU'(U);  dW2_r = Z^T dY;  db2 = sum dY
+//              dH_r = dU W1_r^T;  dW1_r = H^T dU;  db1 = sum dU
+//   ATTN bwd:  dC = dH Wo_r^T;  dWo_r = C^T dH;  dbo = sum dH
+//              D = rowsum(dC * C);  dS = P * (dC V^T - D) / sqrt(d)
+//              dV = P^T dC;  dQ = dS K;  dK = dS^T Q   (written into dQKV)
+//              dX_r = dQKV Wqkv_r^T;  dWqkv_r = X^T dQKV;  db_qkv = sum dQKV
+// The replicated output bias and the residual (and the residual gradient)
+// are added after the all-reduce, by tp_reduce_partials (paper-graph page,
+// "Computation Optimizations": bias + dropout + residual add, fused).
+
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <mutex>
+#include <type_traits>
+#include <vector>
+
+#include "../../include/tp_layer.h"
+#include "aux_kernels.hpp"
+#include "gemm.hpp"
+
+using namespace tpl;
+
+namespace {
+
+thread_local char g_hip_err[256] = "";
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_err, sizeof(g_hip_err), "HIP error %d: %s", (int)e, hipGetErrorString(e));
+  return TP_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// kernel roles (one kernel symbol per GEMM of the layer) and profiling
+// ---------------------------------------------------------------------------
+
+enum Role : int {
+  R_QKV_FWD, R_SCORES, R_SOFTMAX, R_PV, R_O_FWD, R_FC1_FWD, R_FC2_FWD,
+  R_FC2_DGRAD, R_FC2_WGRAD, R_DB2, R_FC1_DGRAD, R_FC1_WGRAD, R_DB1,
+  R_O_DGRAD, R_O_WGRAD, R_DBO, R_ROWDOT, R_DS, R_DV, R_DQ, R_DK,
+  R_QKV_DGRAD, R_QKV_WGRAD, R_DBQKV, R_REDUCE, R_GEMM, R_COUNT
+};
+
+const char* const kRoleName[R_COUNT] = {
+  "qkv_fwd", "scores", "softmax", "pv", "o_fwd", "fc1_fwd", "fc2_fwd",
+  "fc2_dgrad", "fc2_wgrad", "db2", "fc1_dgrad", "fc1_wgrad", "db1",
+  "o_dgrad", "o_wgrad", "dbo", "rowdot", "ds", "dv", "dq", "dk",
+  "qkv_dgrad", "qkv_wgrad", "dbqkv", "reduce", "gemm"};
+
+namespace prof {
+struct Rec {
+  int role;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+std::atomic<bool> on{false};
+std::mutex mu;
+std::vector<Rec> recs;
+std::vector<hipEvent_t> pool;
+
+hipEvent_t take() {
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a start event now and a stop event when it goes out of scope,
+// around the kernels enqueued in between (only while profiling is on).
+struct Scope {
+  int role;
+  double flops, bytes;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  Scope(int r, double f, double by, hipStream_t s) : role(r), flops(f), bytes(by), st(s) {
+    if (on.load(std::memory_order_relaxed)) {
+      a = take();
+      if (a) (void)hipEventRecord(a, st);
+    }
+  }
+  ~Scope() {
+    if (!a) return;
+    hipEvent_t b = take();
+    if (!b) return;
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> g(mu);
+    recs.push_back({role, a, b, flops, bytes});
+  }
+};
+}  // namespace prof
+
+// ---------------------------------------------------------------------------
+// dimensions and buffer layout
+// ---------------------------------------------------------------------------
+
+struct Dims {
+  long h, a, s, b, t;
+  int dt;
+  long T, d, ar, hr, fr, q3, z;
+  size_t es;
+};
+
+int check_args(long h, long a, long s, long b, long t, long rank, int dt, int blk) {
+  if (h <= 0 || a <= 0 || s <= 0 || b <= 0 || t <= 0) return TP_EINVAL;
+  if (dt != TP_BF16 && dt != TP_FP32) return TP_EINVAL;
+  if (blk != TP_ATTN && blk != TP_MLP) return TP_EINVAL;
+  if (rank < 0 || rank >= t) return TP_EINVAL;
+  if (h % a != 0 || a % t != 0) return TP_EINVAL;  // heads stay whole on a rank
+  const long d = h / a, hr = h / t;
+  if (s % 16 != 0 || d % 16 != 0 || hr % 16 != 0) return TP_EUNSUPPORTED;
+  // rows and columns are 32-bit in the kernels; batch counts fit a grid dimension
+  if (s * b > (1L << 30) || 4 * h > (1L << 30) || b * (a / t) > 65535) return TP_EUNSUPPORTED;
+  return TP_OK;
+}
+
+Dims make_dims(long h, long a, long s, long b, long t, int dt) {
+  Dims D;
+  D.h = h; D.a = a; D.s = s; D.b = b; D.t = t; D.dt = dt;
+  D.T = s * b; D.d = h / a; D.ar = a / t; D.hr = h / t; D.fr = 4 * h / t; D.q3 = 3 * h / t;
+  D.z = b * D.ar;
+  D.es = dt == TP_BF16 ? 2 : 4;
+  return D;
+}
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Tile configurations.
+using CfgBig = TileCfg<bf16_t, 256, 256, 2, 2>;  // linear GEMMs
+using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
+using CfgF32 = TileCfg<float, 64, 64, 2, 2>;     // fp32 configuration
+
+// Split-K for GEMMs with too few output tiles to fill 256 CUs.
+int choose_splits(long M, long N, long K) {
+  const long tiles = cdivl(M, CfgBig::BM) * cdivl(N, CfgBig::BN);
+  if (tiles >= 160 || K < 2048) return 1;
+  long s = (256 + tiles / 2) / tiles;
+  s = std::min(s, K / 1024);
+  if (s < 2) return 1;
+  const long chunk = cdivl(cdivl(K, s), CfgBig::BK) * CfgBig::BK;
+  return (int)cdivl(K, chunk);
+}
+
+// Causal [s, s] matrices (scores, P, dS) are defined up to the next multiple
+// of the attention tile in every row; all causal GEMMs use this tile.
+int att_tile(int dt) { return dt == TP_BF16 ? CfgMid::BM : CfgF32::BM; }
+
+struct SavedLayout {
+  size_t qkv, p, c, u, z, total;
+};
+SavedLayout saved_layout(const Dims& D, int blk) {
+  SavedLayout L{};
+  size_t o = 0;
+  if (blk == TP_ATTN) {
+    L.qkv = o; o = al(o + (size_t)D.T * D.q3 * D.es);
+    L.p = o;   o = al(o + (size_t)D.z * D.s * D.s * D.es);
+    L.c = o;   o = al(o + (size_t)D.T * D.hr * D.es);
+  } else {
+    L.u = o; o = al(o + (size_t)D.T * D.fr * D.es);
+    L.z = o; o = al(o + (size_t)D.T * D.fr * D.es);
+  }
+  L.total = o;
+  return L;
+}
+
+size_t partial_bytes(const Dims& D, long M, long N, long K) {
+  if (D.dt != TP_BF16) return 0;
+  const int sp = choose_splits(M, N, K);
+  return sp > 1 ? al((size_t)sp * M * N * 4) : 0;
+}
+
+struct WsLayout {
+  size_t s;                 // attn fwd: fp32 scores
+  size_t dc, D, ds, dqkv;   // attn bwd
+  size_t du;                // mlp bwd
+  size_t part, part_bytes;  // split-K partials
+  size_t total;
+};
+WsLayout ws_layout(const Dims& D, int blk) {
+  WsLayout W{};
+  size_t pb = 0;
+  auto upd = [&](long M, long N, long K) { pb = std::max(pb, partial_bytes(D, M, N, K)); };
+  if (blk == TP_ATTN) {
+    upd(D.T, D.q3, D.h); upd(D.T, D.h, D.hr);
+    upd(D.T, D.hr, D.h); upd(D.hr, D.h, D.T); upd(D.T, D.h, D.q3); upd(D.h, D.q3, D.T);
+    const size_t fwd = al((size_t)D.z * D.s * D.s * 4);
+    size_t o = 0;
+    W.dc = o;   o = al(o + (size_t)D.T * D.hr * D.es);
+    W.D = o;    o = al(o + (size_t)D.z * D.s * 4);
+    W.ds = o;   o = al(o + (size_t)D.z * D.s * D.s * D.es);
+    W.dqkv = o; o = al(o + (size_t)D.T * D.q3 * D.es);
+    W.s = 0;
+    W.part = std::max(fwd, o);
+  } else {
+    upd(D.T, D.fr, D.h); upd(D.T, D.h, D.fr);
+    upd(D.T, D.fr, D.h); upd(D.fr, D.h, D.T); upd(D.T, D.h, D.fr); upd(D.h, D.fr, D.T);
+    W.du = 0;
+    W.part = al((size_t)D.T * D.fr * D.es);
+  }
+  W.part_bytes = pb;
+  W.total = W.part + pb;
+  return W;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM dispatch
+// ---------------------------------------------------------------------------
+
+enum Kind { KIND_BIG = 0, KIND_MID = 1 };
+
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE>
+hipError_t launch(GemmArgs p, int batch, hipStream_t st) {
+  p.tiles_m = cdiv(p.M, Cfg::BM);
+  p.tiles_n = cdiv(p.N, Cfg::BN);
+  if (p.group_m <= 0) p.group_m = 8;
+  if (p.zdiv <= 0) p.zdiv = 1;
+  const int tiles = p.tri ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
+  if (tiles == 0 || batch == 0) return hipSuccess;
+  if constexpr (EPI != EPI_SOFTMAX_BWD) {
+    if (p.splits > 1) {
+      p.k_chunk = (int)(cdivl(cdivl(p.K, p.splits), Cfg::BK) * Cfg::BK);
+      hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI_PARTIAL, float, ROLE>), dim3(tiles, p.splits, 1),
+                         dim3(Cfg::NT), 0, st, p);
+      const long n4 = (long)p.M * p.N / 4;
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI, typename Cfg::T, TO, ROLE>), dim3((unsigned)cdivl(n4, 256)),
+                         dim3(256), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI, TO, ROLE>), dim3(tiles, 1, batch), dim3(Cfg::NT), 0, st, p);
+  return hipGetLastError();
+}
+
+// One GEMM call site of the layer: fixed operand layout, epilogue and role;
+// the element type comes from the call's dtype.
+template <bool AK, bool BKM, int EPI, int ROLE, int KIND, bool OUTF32 = false>
+hipError_t run(const Dims& D, GemmArgs p, int batch, hipStream_t st) {
+  if (D.dt == TP_FP32) {
+    p.splits = 1;
+    return launch<CfgF32, AK, BKM, EPI, float, 0>(p, batch, st);
+  }
+  if constexpr (KIND == KIND_BIG) {
+    return launch<CfgBig, AK, BKM, EPI, bf16_t, ROLE>(p, batch, st);
+  } else {
+    p.splits = 1;
+    return launch<CfgMid, AK, BKM, EPI, std::conditional_t<OUTF32, float, bf16_t>, ROLE>(p, batch, st);
+  }
+}
+
+GemmArgs gargs(long M, long N, long K) {
+  GemmArgs p;
+  memset(&p, 0, sizeof(p));
+  p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.zdiv = 1; p.alpha = 1.0f; p.splits = 1; p.group_m = 8;
+  return p;
+}
+
+// Linear (weight) GEMM M x N x K: split-K chosen for the bf16 path.
+template <bool AK, bool BKM, int EPI, int ROLE>
+hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
+  const double extra = (EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD || p.resid) ? 1.0 : 0.0;
+  prof::Scope sc(ROLE, 2.0 * p.M * p.N * p.K,
+                 (double)D.es * ((double)p.M * p.K + (double)p.K * p.N + (1.0 + extra) * p.M * p.N), st);
+  if (D.dt == TP_BF16) {
+    p.splits = choose_splits(p.M, p.N, p.K);
+    p.part = part;
+  }
+  return run<AK, BKM, EPI, ROLE, KIND_BIG>(D, p, 1, st);
+}
+
+template <int ROLE>
+hipError_t colsum(const Dims& D, const void* X, void* out, long R, long N, long ld, hipStream_t st) {
+  prof::Scope sc(ROLE, (double)R * N, (double)D.es * (R * N + N), st);
+  const int vec = D.dt == TP_BF16 ? 8 : 4;
+  const unsigned blocks = (unsigned)cdivl(N, 8L * vec);
+  if (D.dt == TP_BF16)
+    hipLaunchKernelGGL(colsum_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)X, (bf16_t*)out, (int)R,
+                       (int)N, ld);
+  else
+    hipLaunchKernelGGL(colsum_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)X, (float*)out, (int)R,
+                       (int)N, ld);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t softmax_t(const Dims& D, const float* S, void* P, hipStream_t st) {
+  const long rows = D.z * D.s;
+  const unsigned blocks = (unsigned)cdivl(rows, 4);
+  const int pad = att_tile(D.dt);
+  if (D.s <= 2048)
+    hipLaunchKernelGGL((causal_softmax_kernel<T, 8>), dim3(blocks), dim3(256), 0, st, S, (T*)P, rows, (int)D.s, pad);
+  else
+    hipLaunchKernelGGL((causal_softmax_long_kernel<T>), dim3(blocks), dim3(256), 0, st, S, (T*)P, rows, (int)D.s, pad);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t rowdot_t(const Dims& D, const void* dC, const void* C, float* Dv, hipStream_t st) {
+  const long n = D.T * D.ar;
+  hipLaunchKernelGGL(rowdot_kernel<T>, dim3((unsigned)cdivl(n, 256)), dim3(256), 0, st, (const T*)dC, (const T*)C, Dv,
+                     (int)D.T, (int)D.b, (int)D.ar, (int)D.d, (int)D.s);
+  return hipGetLastError();
+}
+
+#define TRY(x)                                 \
+  do {                                         \
+    hipError_t e_ = (x);                       \
+    if (e_ != hipSuccess) return hip_fail(e_); \
+  } while (0)
+
+char* B8(void* p, size_t off) { return static_cast<char*>(p) + off; }
+const char* B8(const void* p, size_t off) { return static_cast<const char*>(p) + off; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Algorithmic cost of one batched attention product over z (sequence, head)
+// pairs: model FLOPs count the full s x s square (Eq. 3 of the paper-graph
+// page); bytes count the lower triangle of the s x s operand / result.
+double att_flops(const Dims& D) { return 2.0 * D.z * D.s * D.s * D.d; }
+double tri_elems(const Dims& D) { return (double)D.z * D.s * (D.s + 1) / 2.0; }
+
+// ---------------------------------------------------------------------------
+// attention block
+// ---------------------------------------------------------------------------
+
+int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, void* saved, void* ws,
+             hipStream_t st) {
+  const SavedLayout S = saved_layout(D, TP_ATTN);
+  const WsLayout W = ws_layout(D, TP_ATTN);
+  void* qkv = B8(saved, S.qkv);
+  void* P = B8(saved, S.p);
+  void* C = B8(saved, S.c);
+  float* scores = reinterpret_cast<float*>(B8(ws, W.s));
+  float* part = reinterpret_cast<float*>(B8(ws, W.part));
+  const double es = (double)D.es, sde = (double)D.z * D.s * D.d * es;
+
+  {  // QKV_r = X Wqkv_r + b_qkv_r
+    GemmArgs p = gargs(D.T, D.q3, D.h);
+    p.A = x; p.lda = D.h;
+    p.B = w->w_in; p.ldb = D.q3;
+    p.C = qkv; p.ldc = D.q3;
+    p.bias = w->b_in;
+    TRY((linear<true, false, EPI_LINEAR, R_QKV_FWD>(D, p, part, st)));
+  }
+  {  // S_z = Q_z K_z^T / sqrt(d), lower-triangular tiles, fp32
+    prof::Scope sc(R_SCORES, att_flops(D), 2 * sde + 4.0 * tri_elems(D), st);
+    GemmArgs p = gargs(D.s, D.s, D.d);
+    p.zdiv = (int)D.ar;
+    p.A = qkv; p.lda = D.b * D.q3; p.a_s1 = D.q3; p.a_s2 = D.d;
+    p.B = B8(qkv, (size_t)D.hr * D.es); p.ldb = D.b * D.q3; p.b_s1 = D.q3; p.b_s2 = D.d;
+    p.C = scores; p.ldc = D.s; p.c_s1 = D.ar * D.s * D.s; p.c_s2 = D.s * D.s;
+    p.alpha = (float)(1.0 / std::sqrt((double)D.d));
+    p.tri = 1;
+    TRY((run<true, true, EPI_LINEAR, R_SCORES, KIND_MID, true>(D, p, (int)D.z, st)));
+  }
+  {  // P = causal softmax(S)
+    prof::Scope sc(R_SOFTMAX, 0.0, (4.0 + es) * tri_elems(D), st);
+    if (D.dt == TP_BF16) TRY(softmax_t<bf16_t>(D, scores, P, st));
+    else TRY(softmax_t<float>(D, scores, P, st));
+  }
+  {  // C_z = P_z V_z (keys <= query)
+    prof::Scope sc(R_PV, att_flops(D), es * tri_elems(D) + 2 * sde, st);
+    GemmArgs p = gargs(D.s, D.d, D.s);
+    p.zdiv = (int)D.ar;
+    p.A = P; p.lda = D.s; p.a_s1 = D.ar * D.s * D.s; p.a_s2 = D.s * D.s;
+    p.B = B8(qkv, (size_t)2 * D.hr * D.es); p.ldb = D.b * D.q3; p.b_s1 = D.q3; p.b_s2 = D.d;
+    p.C = C; p.ldc = D.b * D.hr; p.c_s1 = D.hr; p.c_s2 = D.d;
+    p.kmode = K_LOWER;
+    TRY((run<true, false, EPI_LINEAR, R_PV, KIND_MID>(D, p, (int)D.z, st)));
+  }
+  {  // partial = C Wo_r
+    GemmArgs p = gargs(D.T, D.h, D.hr);
+    p.A = C; p.lda = D.hr;
+    p.B = w->w_out; p.ldb = D.h;
+    p.C = y; p.ldc = D.h;
+    TRY((linear<true, false, EPI_LINEAR, R_O_FWD>(D, p, part, st)));
+  }
+  return TP_OK;
+}
+
+int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void* saved, const void* dy, void* dx,
+             const tp_block_grads* g, void* ws, hipStream_t st) {
+  const SavedLayout S = saved_layout(D, TP_ATTN);
+  const WsLayout W = ws_layout(D, TP_ATTN);
+  const void* qkv = B8(saved, S.qkv);
+  const void* P = B8(saved, S.p);
+  const void* C = B8(saved, S.c);
+  void* dC = B8(ws, W.dc);
+  float* Dv = reinterpret_cast<float*>(B8(ws, W.D));
+  void* dS = B8(ws, W.ds);
+  void* dqkv = B8(ws, W.dqkv);
+  float* part = reinterpret_cast<float*>(B8(ws, W.part));
+  const float scale = (float)(1.0 / std::sqrt((double)D.d));
+  const double es = (double)D.es, sde = (double)D.z * D.s * D.d * es;
+
+  {  // dC = dH Wo_r^T
+    GemmArgs p = gargs(D.T, D.hr, D.h);
+    p.A = dy; p.lda = D.h;
+    p.B = w->w_out; p.ldb = D.h;
+    p.C = dC; p.ldc = D.hr;
+    TRY((linear<true, true, EPI_LINEAR, R_O_DGRAD>(D, p, part, st)));
+  }
+  {  // dWo_r = C^T dH
+    GemmArgs p = gargs(D.hr, D.h, D.T);
+    p.A = C; p.lda = D.hr;
+    p.B = dy; p.ldb = D.h;
+    p.C = g->dw_out; p.ldc = D.h;
+    TRY((linear<false, false, EPI_LINEAR, R_O_WGRAD>(D, p, part, st)));
+  }
+  TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, st));  // dbo (replica)
+  {  // D = rowsum(dC * C) per (sequence, head, query)
+    prof::Scope sc(R_ROWDOT, 2.0 * D.T * D.hr, 2.0 * D.T * D.hr * es + 4.0 * D.z * D.s, st);
+    if (D.dt == TP_BF16) TRY(rowdot_t<bf16_t>(D, dC, C, Dv, st));
+    else TRY(rowdot_t<float>(D, dC, C, Dv, st));
+  }
+  {  // dS = P * (dC V^T - D) / sqrt(d), lower-triangular tiles
+    prof::Scope sc(R_DS, att_flops(D), 2 * sde + 2 * es * tri_elems(D) + 4.0 * D.z * D.s, st);
+    GemmArgs p = gargs(D.s, D.s, D.d);
+    p.zdiv = (int)D.ar;
+    p.A = dC; p.lda = D.b * D.hr; p.a_s1 = D.hr; p.a_s2 = D.d;
+    p.B = B8(qkv, (size_t)2 * D.hr * D.es); p.ldb = D.b * D.q3; p.b_s1 = D.q3; p.b_s2 = D.d;
+    p.C = dS; p.ldc = D.s; p.c_s1 = D.ar * D.s * D.s; p.c_s2 = D.s * D.s;
+    p.aux = P; p.ldx = D.s; p.x_s1 = D.ar * D.s * D.s; p.x_s2 = D.s * D.s;
+    p.rowv = Dv; p.r_s1 = D.ar * D.s; p.r_s2 = D.s;
+    p.alpha = scale;
+    p.tri = 1;
+    TRY((run<true, true, EPI_SOFTMAX_BWD, R_DS, KIND_MID>(D, p, (int)D.z, st)));
+  }
+  {  // dV = P^T dC  (queries >= key)
+    prof::Scope sc(R_DV, att_flops(D), es * tri_elems(D) + 2 * sde, st);
+    GemmArgs p = gargs(D.s, D.d, D.s);
+    p.zdiv = (int)D.ar;
+    p.A = P; p.lda = D.s; p.a_s1 = D.ar * D.s * D.s; p.a_s2 = D.s * D.s;
+    p.B = dC; p.ldb = D.b * D.hr; p.b_s1 = D.hr; p.b_s2 = D.d;
+    p.C = B8(dqkv, (size_t)2 * D.hr * D.es); p.ldc = D.b * D.q3; p.c_s1 = D.q3; p.c_s2 = D.d;
+    p.kmode = K_UPPER;
+    TRY((run<false, false, EPI_LINEAR, R_DV, KIND_MID>(D, p, (int)D.z, st)));
+  }
+  {  // dQ = dS K  (keys <= query); 1/sqrt(d) already in dS
+    prof::Scope sc(R_DQ, att_flops(D), es * tri_elems(D) + 2 * sde, st);
+    GemmArgs p = gargs(D.s, D.d, D.s);
+    p.zdiv = (int)D.ar;
+    p.A = dS; p.lda = D.s; p.a_s1 = D.ar * D.s * D.s; p.a_s2 = D.s * D.s;
+    p.B = B8(qkv, (size_t)D.hr * D.es); p.ldb = D.b * D.q3; p.b_s1 = D.q3; p.b_s2 = D.d;
+    p.C = dqkv; p.ldc = D.b * D.q3; p.c_s1 = D.q3; p.c_s2 = D.d;
+    p.kmode = K_LOWER;
+    TRY((run<true, false, EPI_LINEAR, R_DQ, KIND_MID>(D, p, (int)D.z, st)));
+  }
+  {  // dK = dS^T Q  (queries >= key)
+    prof::Scope sc(R_DK, att_flops(D), es * tri_elems(D) + 2 * sde, st);
+    GemmArgs p = gargs(D.s, D.d, D.s);
+    p.zdiv = (int)D.ar;
+    p.A = dS; p.lda = D.s; p.a_s1 = D.ar * D.s * D.s; p.a_s2 = D.s * D.s;
+    p.B = qkv; p.ldb = D.b * D.q3; p.b_s1 = D.q3; p.b_s2 = D.d;
+    p.C = B8(dqkv, (size_t)D.hr * D.es); p.ldc = D.b * D.q3; p.c_s1 = D.q3; p.c_s2 = D.d;
+    p.kmode = K_UPPER;
+    TRY((run<false, false, EPI_LINEAR, R_DK, KIND_MID>(D, p, (int)D.z, st)));
+  }
+  {  // dX_r = dQKV Wqkv_r^T
+    GemmArgs p = gargs(D.T, D.h, D.q3);
+    p.A = dqkv; p.lda = D.q3;
+    p.B = w->w_in; p.ldb = D.q3;
+    p.C = dx; p.ldc = D.h;
+    TRY((linear<true, true, EPI_LINEAR, R_QKV_DGRAD>(D, p, part, st)));
+  }
+  {  // dWqkv_r = X^T dQKV
+    GemmArgs p = gargs(D.h, D.q3, D.T);
+    p.A = x; p.lda = D.h;
+    p.B = dqkv; p.ldb = D.q3;
+    p.C = g->dw_in; p.ldc = D.q3;
+    TRY((linear<false, false, EPI_LINEAR, R_QKV_WGRAD>(D, p, part, st)));
+  }
+  TRY(colsum<R_DBQKV>(D, dqkv, g->db_in, D.T, D.q3, D.q3, st));
+  return TP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// MLP block
+// ---------------------------------------------------------------------------
+
+int mlp_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, void* saved, void* ws, hipStream_t st) {
+  const SavedLayout S = saved_layout(D, TP_MLP);
+  const WsLayout W = ws_layout(D, TP_MLP);
+  void* U = B8(saved, S.u);
+  void* Z = B8(saved, S.z);
+  float* part = reinterpret_cast<float*>(B8(ws, W.part));
+  {  // U = H W1_r + b1_r; Z = GELU(U)
+    GemmArgs p = gargs(D.T, D.fr, D.h);
+    p.A = x; p.lda = D.h;
+    p.B = w->w_in; p.ldb = D.fr;
+    p.C = U; p.ldc = D.fr;
+    p.C2 = Z; p.ldc2 = D.fr;
+    p.bias = w->b_in;
+    TRY((linear<true, false, EPI_BIAS_GELU, R_FC1_FWD>(D, p, part, st)));
+  }
+  {  // partial = Z W2_r
+    GemmArgs p = gargs(D.T, D.h, D.fr);
+    p.A = Z; p.lda = D.fr;
+    p.B = w->w_out; p.ldb = D.h;
+    p.C = y; p.ldc = D.h;
+    TRY((linear<true, false, EPI_LINEAR, R_FC2_FWD>(D, p, part, st)));
+  }
+  return TP_OK;
+}
+
+int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void* saved, const void* dy, void* dx,
+            const tp_block_grads* g, void* ws, hipStream_t st) {
+  const SavedLayout S = saved_layout(D, TP_MLP);
+  const WsLayout W = ws_layout(D, TP_MLP);
+  const void* U = B8(saved, S.u);
+  const void* Z = B8(saved, S.z);
+  void* dU = B8(ws, W.du);
+  float* part = reinterpret_cast<float*>(B8(ws, W.part));
+  {  // dU = (dY W2_r^T) * GELU'(U)
+    GemmArgs p = gargs(D.T, D.fr, D.h);
+    p.A = dy; p.lda = D.h;
+    p.B = w->w_out; p.ldb = D.h;
+    p.C = dU; p.ldc = D.fr;
+    p.aux = U; p.ldx = D.fr;
+    TRY((linear<true, true, EPI_GELU_BWD, R_FC2_DGRAD>(D, p, part, st)));
+  }
+  {  // dW2_r = Z^T dY
+    GemmArgs p = gargs(D.fr, D.h, D.T);
+    p.A = Z; p.lda = D.fr;
+    p.B = dy; p.ldb = D.h;
+    p.C = g->dw_out; p.ldc = D.h;
+    TRY((linear<false, false, EPI_LINEAR, R_FC2_WGRAD>(D, p, part, st)));
+  }
+  TRY(colsum<R_DB2>(D, dy, g->db_out, D.T, D.h, D.h, st));  // db2 (replica)
+  {  // dH_r = dU W1_r^T
+    GemmArgs p = gargs(D.T, D.h, D.fr);
+    p.A = dU; p.lda = D.fr;
+    p.B = w->w_in; p.ldb = D.fr;
+    p.C = dx; p.ldc = D.h;
+    TRY((linear<true, true, EPI_LINEAR, R_FC1_DGRAD>(D, p, part, st)));
+  }
+  {  // dW1_r = H^T dU
+    GemmArgs p = gargs(D.h, D.fr, D.T);
+    p.A = x; p.lda = D.h;
+    p.B = dU; p.ldb = D.fr;
+    p.C = g->dw_in; p.ldc = D.fr;
+    TRY((linear<false, false, EPI_LINEAR, R_FC1_WGRAD>(D, p, part, st)));
+  }
+  TRY(colsum<R_DB1>(D, dU, g->db_in, D.T, D.fr, D.fr, st));
+  return TP_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+int tp_check_args(int h, int a, int s, int b, int t, int rank, int dtype, int block) {
+  return check_args(h, a, s, b, t, rank, dtype, block);
+}
+
+size_t tp_saved_bytes(int h, int a, int s, int b, int t, int dtype, int block) {
+  if (check_args(h, a, s, b, t, 0, dtype, block) != TP_OK) return 0;
+  return saved_layout(make_dims(h, a, s, b, t, dtype), block).total;
+}
+
+size_t tp_workspace_bytes(int h, int a, int s, int b, int t, int dtype, int block) {
+  if (check_args(h, a, s, b, t, 0, dtype, block) != TP_OK) return 0;
+  return ws_layout(make_dims(h, a, s, b, t, dtype), block).total;
+}
+
+int tp_layer_fwd(int h, int a, int s, int b, int t, int rank, int dtype, int block, const void* x,
+                 const tp_block_weights* w, void* y_partial, void* saved, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int rc = check_args(h, a, s, b, t, rank, dtype, block);
+  if (rc != TP_OK) return rc;
+  if (!x || !w || !w->w_in || !w->b_in || !w->w_out || !y_partial || !saved || !workspace) return TP_ENULL;
+  if (misaligned(x) || misaligned(w->w_in) || misaligned(w->b_in) || misaligned(w->w_out) || misaligned(y_partial) ||
+      misaligned(saved) || misaligned(workspace))
+    return TP_EALIGN;
+  const Dims D = make_dims(h, a, s, b, t, dtype);
+  if (workspace_bytes < ws_layout(D, block).total) return TP_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return block == TP_ATTN ? attn_fwd(D, x, w, y_partial, saved, workspace, st)
+                          : mlp_fwd(D, x, w, y_partial, saved, workspace, st);
+}
+
+int tp_layer_bwd(int h, int a, int s, int b, int t, int rank, int dtype, int block, const void* x,
+                 const tp_block_weights* w, const void* saved, const void* dy, void* dx_partial,
+                 const tp_block_grads* g, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_args(h, a, s, b, t, rank, dtype, block);
+  if (rc != TP_OK) return rc;
+  if (!x || !w || !w->w_in || !w->w_out || !saved || !dy || !dx_partial || !g || !g->dw_in || !g->db_in ||
+      !g->dw_out || !g->db_out || !workspace)
+    return TP_ENULL;
+  if (misaligned(x) || misaligned(w->w_in) || misaligned(w->w_out) || misaligned(saved) || misaligned(dy) ||
+      misaligned(dx_partial) || misaligned(g->dw_in) || misaligned(g->db_in) || misaligned(g->dw_out) ||
+      misaligned(g->db_out) || misaligned(workspace))
+    return TP_EALIGN;
+  const Dims D = make_dims(h, a, s, b, t, dtype);
+  if (workspace_bytes < ws_layout(D, block).total) return TP_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return block == TP_ATTN ? attn_bwd(D, x, w, saved, dy, dx_partial, g, workspace, st)
+                          : mlp_bwd(D, x, w, saved, dy, dx_partial, g, workspace, st);
+}
+
+int tp_reduce_partials(int dtype, long rows, long cols, int t, const void* partials, const void* bias,
+                       const void* residual, void* out, void* stream) {
+  if (dtype != TP_BF16 && dtype != TP_FP32) return TP_EINVAL;
+  if (t <= 0 || rows < 0 || cols <= 0 || cols % 8 != 0) return TP_EINVAL;
+  if (!partials || !out) return TP_ENULL;
+  if (misaligned(partials) || misaligned(out) || misaligned(bias) || misaligned(residual)) return TP_EALIGN;
+  if (rows == 0) return TP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long n = rows * cols;
+  const size_t es = dtype == TP_BF16 ? 2 : 4;
+  prof::Scope sc(R_REDUCE, (double)t * n, (double)es * n * (t + 1 + (residual ? 1 : 0)), st);
+  const unsigned blocks = (unsigned)cdivl(n / 4, 256);
+  if (dtype == TP_BF16)
+    hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)partials,
+                       (const bf16_t*)bias, (const bf16_t*)residual, (bf16_t*)out, rows, cols, t);
+  else
+    hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)partials,
+                       (const float*)bias, (const float*)residual, (float*)out, rows, cols, t);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TP_OK : hip_fail(e);
+}
+
+int tp_gemm(int dtype, int M, int N, int K, float alpha, const void* A, long lda, int a_kmajor, const void* B, long ldb,
+            int b_kmajor, const void* bias, void* C, long ldc, void* stream) {
+  if (dtype != TP_BF16 && dtype != TP_FP32) return TP_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0) return TP_EINVAL;
+  if (M % 16 || N % 16 || K % 16 || lda % 8 || ldb % 8 || ldc % 8) return TP_EUNSUPPORTED;
+  if (lda < (a_kmajor ? K : M) || ldb < (b_kmajor ? K : N) || ldc < N) return TP_EINVAL;
+  if (!A || !B || !C) return TP_ENULL;
+  if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias)) return TP_EALIGN;
+  const Dims D = make_dims(16, 1, 16, 1, 1, dtype);  // only the dtype is used
+  GemmArgs p = gargs(M, N, K);
+  p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C; p.ldc = ldc;
+  p.bias = bias; p.alpha = alpha;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  prof::Scope sc(R_GEMM, 2.0 * M * N * K, (double)D.es * ((double)M * K + (double)K * N + (double)M * N), st);
+  hipError_t e;
+  if (a_kmajor && !b_kmajor) e = run<true, false, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
+  else if (a_kmajor && b_kmajor) e = run<true, true, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
+  else if (!a_kmajor && !b_kmajor) e = run<false, false, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
+  else e = run<false, true, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
+  return e == hipSuccess ? TP_OK : hip_fail(e);
+}
+
+int tp_prof_enable(int on) {
+  std::lock_guard<std::mutex> g(prof::mu);
+  if (on) {
+    for (auto& r : prof::recs) {
+      prof::pool.push_back(r.a);
+      prof::pool.push_back(r.b);
+    }
+    prof::recs.clear();
+  }
+  prof::on.store(on != 0);
+  return TP_OK;
+}
+
+int tp_prof_read(tp_prof_entry* out, int max_entries) {
+  if (!out && max_entries > 0) return TP_ENULL;
+  std::vector<prof::Rec> recs;
+  {
+    std::lock_guard<std::mutex> g(prof::mu);
+    recs.swap(prof::recs);
+  }
+  tp_prof_entry acc[R_COUNT];
+  memset(acc, 0, sizeof(acc));
+  int err = TP_OK;
+  for (auto& r : recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) err = hip_fail(e);
+    tp_prof_entry& a = acc[r.role];
+    a.launches += 1;
+    a.ms += ms;
+    a.flops += r.flops;
+    a.bytes += r.bytes;
+  }
+  {
+    std::lock_guard<std::mutex> g(prof::mu);
+    for (auto& r : recs) {
+      prof::pool.push_back(r.a);
+      prof::pool.push_back(r.b);
+    }
+  }
+  if (err != TP_OK) return err;
+  int n = 0;
+  for (int i = 0; i < R_COUNT; ++i) {
+    if (acc[i].launches == 0) continue;
+    if (n < max_entries) {
+      out[n] = acc[i];
+      snprintf(out[n].name, sizeof(out[n].name), "%s", kRoleName[i]);
+    }
+    ++n;
+  }
+  return n;
+}
+
+const char* tp_strerror(int code) {
+  switch (code) {
+    case TP_OK: return "ok";
+    case TP_EINVAL: return "invalid argument (dims, heads not divisible by t, rank out of range, or bad enum)";
+    case TP_EUNSUPPORTED: return "unsupported shape (s, d and h/t must be multiples of 16)";
+    case TP_ENULL: return "a required pointer is NULL";
+    case TP_EALIGN: return "a pointer is not 16-byte aligned";
+    case TP_EWORKSPACE: return "workspace smaller than tp_workspace_bytes()";
+    case TP_EHIP: return g_hip_err[0] ? g_hip_err : "HIP error";
+  }
+  return "unknown error code";
+}
+
+}  // extern "C"

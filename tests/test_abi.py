@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and validates arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from megatron_tensor_layer_amd import tplayer as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_layer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tp.LIB_PATH), reason="libtplayer.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(tp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = tp.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    # the exported symbols are plain C names (no C++ mangling)
+    nm = os.popen(f"nm -D --defined-only {tp.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", nm, re.M), name
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((64, 4, 32, 2, 4, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_OK),
+    ((12288, 96, 2048, 1, 8, 7, tp.TP_BF16, tp.TP_MLP), tp.TP_OK),
+    ((25600, 160, 2048, 1, 8, 3, tp.TP_BF16, tp.TP_ATTN), tp.TP_OK),
+    ((2304, 24, 2048, 4, 1, 0, tp.TP_BF16, tp.TP_ATTN), tp.TP_OK),
+    ((64, 4, 32, 2, 3, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EINVAL),      # a % t != 0: heads must stay whole
+    ((64, 5, 32, 2, 1, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EINVAL),      # h % a != 0
+    ((64, 4, 32, 2, 4, 4, tp.TP_FP32, tp.TP_ATTN), tp.TP_EINVAL),      # rank out of range
+    ((64, 4, 32, 2, 4, -1, tp.TP_FP32, tp.TP_ATTN), tp.TP_EINVAL),
+    ((64, 4, 0, 2, 4, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EINVAL),
+    ((64, 4, 32, 2, 4, 0, 7, tp.TP_ATTN), tp.TP_EINVAL),
+    ((64, 4, 32, 2, 4, 0, tp.TP_FP32, 2), tp.TP_EINVAL),
+    ((64, 4, 24, 2, 4, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EUNSUPPORTED),  # s % 16
+    ((96, 4, 32, 2, 4, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EUNSUPPORTED),  # d = 24
+    ((128, 8, 32, 2, 8, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_OK),           # d = 16, h/t = 16
+])
+def test_check_args(args, expect):
+    assert tp.tp_check_args(*args) == expect
+
+
+def test_saved_and_workspace_sizes():
+    h, a, s, b, t = 12288, 96, 2048, 1, 8
+    T, ar = s * b, a // t
+    sa = tp.tp_saved_bytes(h, a, s, b, t, tp.TP_BF16, tp.TP_ATTN)
+    sm = tp.tp_saved_bytes(h, a, s, b, t, tp.TP_BF16, tp.TP_MLP)
+    assert sa >= 2 * (T * 3 * h // t + b * ar * s * s + T * h // t)
+    assert sm >= 2 * 2 * T * 4 * h // t
+    assert tp.tp_workspace_bytes(h, a, s, b, t, tp.TP_BF16, tp.TP_ATTN) >= 4 * b * ar * s * s
+    assert tp.tp_saved_bytes(h, a, s, b, 5, tp.TP_BF16, tp.TP_ATTN) == 0  # a % t != 0 -> 0
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_fwd_rejects_null_misaligned_and_small_workspace_on_host():
+    L = tp.lib()
+    dims = (64, 4, 32, 2, 4, 0, tp.TP_FP32, tp.TP_ATTN)
+    ok = tp.TPBlockWeights(0x10000, 0x20000, 0x30000, 0x40000)
+    none = ctypes.c_void_p(None)
+    a = _fake(0x100000)
+    ws_need = tp.tp_workspace_bytes(64, 4, 32, 2, 4, tp.TP_FP32, tp.TP_ATTN)
+    # NULL input
+    assert L.tp_layer_fwd(*dims, none, ctypes.byref(ok), a, a, a, ws_need, none) == tp.TP_ENULL
+    # NULL weight pointer
+    bad = tp.TPBlockWeights(0x10000, None, 0x30000, 0x40000)
+    assert L.tp_layer_fwd(*dims, a, ctypes.byref(bad), a, a, a, ws_need, none) == tp.TP_ENULL
+    # misaligned
+    assert L.tp_layer_fwd(*dims, _fake(0x100004), ctypes.byref(ok), a, a, a, ws_need, none) == tp.TP_EALIGN
+    # workspace too small
+    assert L.tp_layer_fwd(*dims, a, ctypes.byref(ok), a, a, a, ws_need - 1, none) == tp.TP_EWORKSPACE
+    # invalid dims come first
+    assert L.tp_layer_fwd(64, 4, 32, 2, 3, 0, tp.TP_FP32, tp.TP_ATTN, none, None, none, none, none, 0,
+                          none) == tp.TP_EINVAL
+
+
+def test_bwd_rejects_null_grads_on_host():
+    L = tp.lib()
+    dims = (64, 4, 32, 2, 4, 1, tp.TP_FP32, tp.TP_MLP)
+    ok = tp.TPBlockWeights(0x10000, 0x20000, 0x30000, 0x40000)
+    g = tp.TPBlockGrads(0x50000, 0x60000, None, 0x80000)
+    a = _fake(0x100000)
+    ws = tp.tp_workspace_bytes(64, 4, 32, 2, 4, tp.TP_FP32, tp.TP_MLP)
+    assert L.tp_layer_bwd(*dims, a, ctypes.byref(ok), a, a, a, ctypes.byref(g), a, ws, None) == tp.TP_ENULL
+
+
+def test_reduce_and_gemm_validation_on_host():
+    L = tp.lib()
+    a = _fake(0x100000)
+    none = ctypes.c_void_p(None)
+    assert L.tp_reduce_partials(tp.TP_BF16, 4, 12, 2, a, none, none, a, None) == tp.TP_EINVAL   # cols % 8
+    assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, none, none, none, a, None) == tp.TP_ENULL
+    assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, _fake(0x100002), none, none, a, None) == tp.TP_EALIGN
+    assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, a, _fake(0x100008), none, a, None) == tp.TP_EALIGN
+    assert L.tp_gemm(tp.TP_BF16, 20, 16, 16, 1.0, a, 16, 1, a, 16, 1, None, a, 16, None) == tp.TP_EUNSUPPORTED
+    assert L.tp_gemm(tp.TP_BF16, 16, 16, 32, 1.0, a, 16, 1, a, 32, 1, None, a, 16, None) == tp.TP_EINVAL  # lda < K
+
+
+def test_profiler_without_gpu_work():
+    tp.tp_prof_enable(True)
+    assert tp.tp_prof_read() == {}
+    tp.tp_prof_enable(False)
+
+
+def test_strerror():
+    for code in (tp.TP_OK, tp.TP_EINVAL, tp.TP_EUNSUPPORTED, tp.TP_ENULL, tp.TP_EALIGN, tp.TP_EWORKSPACE, tp.TP_EHIP):
+        assert len(tp.strerror(code)) > 0
+    assert "unknown" in tp.strerror(-99)

@@ -1,0 +1,272 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.  Tolerance per tensor: max|gpu - ref| / max|ref| <= 1e-5
+for the fp32 configuration and <= 1e-2 for bf16."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from megatron_tensor_layer_amd import inputs as I
+from megatron_tensor_layer_amd import tplayer as tp
+from megatron_tensor_layer_amd.layer import weights_from_parts
+from oracle import tp_layer_oracle as O
+
+from gpu_helpers import (TOL, assert_close, compare_full_layer, dtype_code, full_layer_gpu, full_layer_oracle,
+                         rel_err, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(gpu):
+    tp.lib()  # fail loudly if the library is missing on a GPU machine
+    yield
+
+
+# ---------------------------------------------------------------------------
+# the MFMA GEMM on its own, every operand layout, ragged tiles
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("ak,bk", [(1, 0), (1, 1), (0, 0), (0, 1)])
+@pytest.mark.parametrize("M,N,K", [(272, 400, 336), (16, 32, 48), (528, 256, 1040)])
+def test_gemm_layouts(dtype, ak, bk, M, N, K):
+    print(f"gemm {dtype} ak={ak} bk={bk} {M}x{N}x{K}", flush=True)
+    cfg = I.make_config("gemm", 64, 4, 32, 2, 1, dtype)
+    rng = np.random.default_rng(M * 7 + N * 3 + K + ak * 2 + bk)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((K, N)).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    if dtype == "bf16":
+        A, B, bias = I.round_to_bf16(A), I.round_to_bf16(B), I.round_to_bf16(bias)
+    ref = 0.5 * (A.astype(np.float64) @ B.astype(np.float64)) + bias
+    Ad = to_dev(A if ak else A.T, cfg)
+    Bd = to_dev(B.T if bk else B, cfg)
+    C = torch.full((M, N), float("nan"), device="cuda", dtype=tp.torch_dtype(dtype_code(cfg)))
+    tp.tp_gemm(dtype_code(cfg), M, N, K, 0.5, Ad, K if ak else M, ak, Bd, K if bk else N, bk, to_dev(bias, cfg), C, N)
+    torch.cuda.synchronize()
+    # bf16 output rounding (2^-9) plus fp32 accumulation; fp32: accumulation only
+    tol = 8e-3 if dtype == "bf16" else 1e-5
+    assert rel_err(to_np(C), ref) <= tol
+
+
+# ---------------------------------------------------------------------------
+# whole layer, all ranks, element by element
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    # the fp32 check configuration: h=64, a=4, s=32, b=2, t=4
+    "check_fp32": I.CONFIGS["check_fp32"],
+    # bf16, several tiles in every GEMM with ragged tails (T=544, s=272 vs 128/256 tiles)
+    "bf16_ragged": I.make_config("bf16_ragged", h=384, a=6, s=272, b=2, t=2, dtype="bf16"),
+    # bf16, d = 160 (non power of two head width, as at the 1T shape), t = 2
+    "bf16_d160": I.make_config("bf16_d160", h=320, a=2, s=160, b=2, t=2, dtype="bf16"),
+    # bf16, d = 96 and t = 1 (as at the 1.7B shape), short-K split-K off
+    "bf16_d96": I.make_config("bf16_d96", h=192, a=2, s=128, b=3, t=1, dtype="bf16"),
+    # bf16, split-K engaged (few output tiles, K = h >= 2048)
+    "bf16_splitk": I.make_config("bf16_splitk", h=2048, a=16, s=256, b=1, t=2, dtype="bf16"),
+    # fp32, ragged and several tiles
+    "fp32_ragged": I.make_config("fp32_ragged", h=128, a=8, s=80, b=3, t=2, dtype="fp32"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_full_layer_against_oracle(name):
+    cfg = SMALL[name]
+    print(f"full layer {name}: {cfg}", flush=True)
+    layer, X, dY = full_layer_gpu(cfg)
+    _, Y, cache, g = full_layer_oracle(cfg, X, dY)
+    report = {}
+    compare_full_layer(cfg, layer, Y, cache, g, TOL[cfg.dtype], report)
+    print({k: f"{v:.2e}" for k, v in report.items()}, flush=True)
+
+
+def test_rank_partials_against_oracle_per_rank():
+    """Each rank's partial outputs and gradients against the oracle's per-rank
+    view (fp32 check configuration)."""
+    cfg = I.CONFIGS["check_fp32"]
+    layer, X, dY = full_layer_gpu(cfg)
+    p = I.params_full(cfg)
+    ar = cfg.a // cfg.t
+    tol = TOL["fp32"]
+    # attention partials of every rank from the same X
+    for r in range(cfg.t):
+        pr = O.shard_params(p, r, cfg.t)
+        part, _ = O.attention_rank_forward(X, pr, cfg.s, cfg.b, ar)
+        out = torch.empty_like(layer.H)
+        layer.block_fwd(tp.TP_ATTN, r, to_dev(X, cfg), out)
+        torch.cuda.synchronize()
+        assert_close(f"attn partial r={r}", to_np(out), part, tol)
+    # MLP partials and their backward from the same (oracle) H
+    H = to_np(layer.H)
+    for r in range(cfg.t):
+        pr = O.shard_params(p, r, cfg.t)
+        part, cm = O.mlp_rank_forward(H, pr)
+        gm = O.mlp_rank_backward(cm, pr, dY)
+        out = torch.empty_like(layer.H)
+        layer.block_fwd(tp.TP_MLP, r, layer.H, out)
+        dx = torch.empty_like(layer.H)
+        layer.block_bwd(tp.TP_MLP, r, layer.H, to_dev(dY, cfg), dx)
+        torch.cuda.synchronize()
+        assert_close(f"mlp partial r={r}", to_np(out), part, tol)
+        assert_close(f"mlp dH partial r={r}", to_np(dx), gm["dH"], tol)
+
+
+def test_layer_is_deterministic():
+    cfg = SMALL["bf16_ragged"]
+    a, _, _ = full_layer_gpu(cfg)
+    b, _, _ = full_layer_gpu(cfg)
+    for x, y in ((a.Y, b.Y), (a.dX, b.dX), (a.grads[1]["attn"][0], b.grads[1]["attn"][0]),
+                 (a.grads[0]["mlp"][1], b.grads[0]["mlp"][1])):
+        assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# full-size shapes, rank 0, in the launch configuration the benchmark times.
+# Causality makes rows sigma < L of the attention block depend only on the
+# first L tokens, and an upstream gradient that is zero for sigma >= L makes
+# every gradient equal to that of the L-token problem; the MLP is token-wise,
+# so any subset of rows can be checked exactly.
+# ---------------------------------------------------------------------------
+
+FULL = ["gpt_1.7b", "gpt_18b", "gpt_175b", "gpt_1t"]
+PREFIX = {"gpt_1.7b": 96, "gpt_18b": 96, "gpt_175b": 96, "gpt_1t": 48}
+
+
+def _zero_beyond(dY, rows):
+    out = dY.copy()
+    out[rows:] = 0.0
+    return out
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_rank0_attention(name):
+    cfg = I.CONFIGS[name]
+    L = PREFIX[name]
+    print(f"full-size attention {name} rank 0, prefix {L}", flush=True)
+    h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    dt = dtype_code(cfg)
+    parts = I.params_rank(cfg, 0)
+    w = weights_from_parts(parts, dt)["attn"]
+    X = I.activation(cfg, "X")
+    Lb = L * b
+    dH = _zero_beyond(I.activation(cfg, "dY"), Lb)
+    Xd, dHd = to_dev(X, cfg), to_dev(dH, cfg)
+    saved = torch.empty(tp.tp_saved_bytes(h, a, s, b, t, dt, tp.TP_ATTN), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tp.tp_workspace_bytes(h, a, s, b, t, dt, tp.TP_ATTN), dtype=torch.uint8, device="cuda")
+    y = torch.full_like(Xd, float("nan"))
+    dx = torch.full_like(Xd, float("nan"))
+    grads = tuple(torch.full(shp, float("nan"), dtype=Xd.dtype, device="cuda")
+                  for shp in tp.block_shapes(h, t, tp.TP_ATTN))
+    tp.tp_layer_fwd(h, a, s, b, t, 0, dt, tp.TP_ATTN, Xd, w, y, saved, ws)
+    tp.tp_layer_bwd(h, a, s, b, t, 0, dt, tp.TP_ATTN, Xd, w, saved, dHd, dx, grads, ws)
+    torch.cuda.synchronize()
+
+    pr = {k: v.astype(np.float64) for k, v in parts.items()}
+    ar = a // t
+    part, cache = O.attention_rank_forward(X[:Lb], pr, L, b, ar)
+    gr = O.attention_rank_backward(cache, pr, dH[:Lb], L, b, ar)
+    tol = TOL[cfg.dtype]
+    yg = to_np(y)
+    assert np.all(np.isfinite(yg))
+    assert_close("partial[:L]", yg[:Lb], part, tol)
+    dxg = to_np(dx)
+    assert_close("dX[:L]", dxg[:Lb], gr["dX"], tol)
+    assert np.all(dxg[Lb:] == 0.0), "dX rows beyond the gradient's support must be exactly zero"
+    assert_close("dWqkv", to_np(grads[0]), np.concatenate([gr["dWq"], gr["dWk"], gr["dWv"]], axis=1), tol)
+    assert_close("dbqkv", to_np(grads[1]), np.concatenate([gr["dbq"], gr["dbk"], gr["dbv"]]), tol)
+    assert_close("dWo", to_np(grads[2]), gr["dWo"], tol)
+    assert_close("dbo", to_np(grads[3]), gr["dbo"], tol)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_rank0_mlp(name):
+    cfg = I.CONFIGS[name]
+    h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    T = s * b
+    print(f"full-size MLP {name} rank 0", flush=True)
+    dt = dtype_code(cfg)
+    parts = I.params_rank(cfg, 0)
+    w = weights_from_parts(parts, dt)["mlp"]
+    Hin = I.activation(cfg, "H")
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, size=61, replace=False)]))
+    dY = np.zeros_like(Hin)
+    dY[rows] = I.activation(cfg, "dY")[rows]
+    Hd, dYd = to_dev(Hin, cfg), to_dev(dY, cfg)
+    saved = torch.empty(tp.tp_saved_bytes(h, a, s, b, t, dt, tp.TP_MLP), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tp.tp_workspace_bytes(h, a, s, b, t, dt, tp.TP_MLP), dtype=torch.uint8, device="cuda")
+    y = torch.full_like(Hd, float("nan"))
+    dx = torch.full_like(Hd, float("nan"))
+    grads = tuple(torch.full(shp, float("nan"), dtype=Hd.dtype, device="cuda")
+                  for shp in tp.block_shapes(h, t, tp.TP_MLP))
+    tp.tp_layer_fwd(h, a, s, b, t, 0, dt, tp.TP_MLP, Hd, w, y, saved, ws)
+    tp.tp_layer_bwd(h, a, s, b, t, 0, dt, tp.TP_MLP, Hd, w, saved, dYd, dx, grads, ws)
+    torch.cuda.synchronize()
+
+    pr = {k: v.astype(np.float64) for k, v in parts.items()}
+    part, cm = O.mlp_rank_forward(Hin[rows], pr)
+    gm = O.mlp_rank_backward(cm, pr, dY[rows])
+    tol = TOL[cfg.dtype]
+    yg = to_np(y)
+    assert np.all(np.isfinite(yg))
+    assert_close("partial[rows]", yg[rows], part, tol)
+    dxg = to_np(dx)
+    assert_close("dH[rows]", dxg[rows], gm["dH"], tol)
+    others = np.setdiff1d(np.arange(T), rows)
+    assert np.all(dxg[others] == 0.0)
+    assert_close("dW1", to_np(grads[0]), gm["dW1"], tol)
+    assert_close("db1", to_np(grads[1]), gm["db1"], tol)
+    assert_close("dW2", to_np(grads[2]), gm["dW2"], tol)
+    assert_close("db2", to_np(grads[3]), gm["db2"], tol)
+
+
+def test_stand_in_reduce_is_the_elementwise_sum():
+    """'parallelism' blog, 'First: the three collectives': [1,2,3,4] + [10,20,30,40]."""
+    for dt in (tp.TP_BF16, tp.TP_FP32):
+        td = tp.torch_dtype(dt)
+        parts = torch.tensor([[[1, 2, 3, 4, 0, 0, 0, 0]], [[10, 20, 30, 40, 0, 0, 0, 0]]], dtype=td, device="cuda")
+        out = torch.empty((1, 8), dtype=td, device="cuda")
+        tp.tp_reduce_partials(dt, parts, out)
+        torch.cuda.synchronize()
+        assert out.float().cpu().tolist() == [[11, 22, 33, 44, 0, 0, 0, 0]]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_reduce_with_bias_and_residual_matches_block_output(dtype):
+    cfg = I.make_config("reduce", 64, 4, 32, 2, 3, dtype)
+    rng = np.random.default_rng(9)
+    rows, cols, t = 200, 72, 3
+    parts = [rng.standard_normal((rows, cols)).astype(np.float32) for _ in range(t)]
+    bias = rng.standard_normal(cols).astype(np.float32)
+    res = rng.standard_normal((rows, cols)).astype(np.float32)
+    if dtype == "bf16":
+        parts = [I.round_to_bf16(x) for x in parts]
+        bias, res = I.round_to_bf16(bias), I.round_to_bf16(res)
+    ref = O.block_output(parts, bias, res)
+    out = torch.empty((rows, cols), dtype=tp.torch_dtype(dtype_code(cfg)), device="cuda")
+    tp.tp_reduce_partials(dtype_code(cfg), to_dev(np.stack(parts), cfg), out, bias=to_dev(bias, cfg),
+                          residual=to_dev(res, cfg))
+    torch.cuda.synchronize()
+    # fp32 sum, one rounding to the storage type
+    assert rel_err(to_np(out), ref) <= (4e-3 if dtype == "bf16" else 1e-6)
+
+
+def test_profiler_attributes_every_role():
+    cfg = SMALL["bf16_ragged"]
+    tp.tp_prof_enable(True)
+    full_layer_gpu(cfg)
+    tp.tp_prof_enable(False)
+    prof = tp.tp_prof_read()
+    roles = {"qkv_fwd", "scores", "softmax", "pv", "o_fwd", "fc1_fwd", "fc2_fwd", "fc2_dgrad", "fc2_wgrad", "db2",
+             "fc1_dgrad", "fc1_wgrad", "db1", "o_dgrad", "o_wgrad", "dbo", "rowdot", "ds", "dv", "dq", "dk",
+             "qkv_dgrad", "qkv_wgrad", "dbqkv", "reduce"}
+    assert roles <= set(prof)
+    for name in roles - {"reduce"}:
+        assert prof[name]["launches"] == cfg.t, name
+        assert prof[name]["ms"] > 0
+    assert prof["reduce"]["launches"] == 4
+    T, h, t = cfg.tokens, cfg.h, cfg.t
+    assert prof["fc1_fwd"]["flops"] == pytest.approx(t * 2.0 * T * (4 * h // t) * h)
