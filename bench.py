@@ -1,0 +1,246 @@
+"""Benchmark: one tensor-parallel rank's share of a GPT layer, forward +
+backward, on one MI355X.
+
+A step is one pass of the whole layer over one batch: the t ranks' calls
+(attention fwd, MLP fwd, MLP bwd, attention bwd) run one after another on
+one GPU, with the stand-in all-reduce (fused with the bias + residual add)
+between the blocks.  The metric is model TFLOP/s per GPU for one rank's
+share:
+
+    F_rank = 72 b s h^2 (1 + s / 6h) / t      (paper-graph page, "FLOP Counting
+                                               and Training Time Estimation",
+                                               Eq. 3 for one layer, no
+                                               recomputation, no logit layer)
+    t_rank = (time of all t ranks' calls, stand-in reductions excluded) / t
+    value  = F_rank / t_rank
+
+Inputs are synthetic and seeded: weights and biases N(0, 0.02^2), X and dY
+N(0, 1), drawn on the GPU by torch's generator and stored in bf16.
+
+    python bench.py [--steps K] [--warmup W] [--config gpt_175b] [--no-cpu-baseline]
+
+Prints one JSON line.  Only one GPU is used: --gpus above 1 is refused.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk x 2.4 GHz (AMD MI355X spec)
+PEAK_HBM_GBPS = 8000.0      # HBM3E, AMD MI355X spec
+DEFAULT_CONFIG = "gpt_175b"
+
+
+def model_flops_per_rank(h, s, b, t):
+    return 72.0 * b * s * h * h * (1.0 + s / (6.0 * h)) / t
+
+
+def build_layer(cfg, seed=1234):
+    import torch
+    from megatron_tensor_layer_amd import tplayer as tp
+    from megatron_tensor_layer_amd.layer import TPLayer
+
+    h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+
+    def rnd(shape, std):
+        x = torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32)
+        return (x * std).to(torch.bfloat16)
+
+    weights = []
+    for _ in range(t):
+        w = {}
+        for name, blk in (("attn", tp.TP_ATTN), ("mlp", tp.TP_MLP)):
+            w[name] = tuple(rnd(shp, 0.02) for shp in tp.block_shapes(h, t, blk))
+        weights.append(w)
+    layer = TPLayer(h, a, s, b, t, tp.TP_BF16, weights)
+    X = rnd((s * b, h), 1.0)
+    dY = rnd((s * b, h), 1.0)
+    return layer, X, dY
+
+
+def timed_steps(layer, X, dY, steps):
+    """Per step: HIP events (torch's current stream, the stream the library
+    launches on) around each block's rank loop and each stand-in reduction."""
+    import torch
+    from megatron_tensor_layer_amd import tplayer as tp
+
+    t = layer.t
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        e = ev[k]
+        e[0].record()
+        for r in range(t):
+            layer.block_fwd(tp.TP_ATTN, r, X, layer.partials[r])
+        e[1].record()
+        layer.reduce(layer.H, layer.weights[0]["attn"][3], X)
+        e[2].record()
+        for r in range(t):
+            layer.block_fwd(tp.TP_MLP, r, layer.H, layer.partials[r])
+        e[3].record()
+        layer.reduce(layer.Y, layer.weights[0]["mlp"][3], layer.H)
+        e[4].record()
+        for r in range(t):
+            layer.block_bwd(tp.TP_MLP, r, layer.H, dY, layer.partials[r])
+        e[5].record()
+        layer.reduce(layer.dH, None, dY)
+        e[6].record()
+        for r in range(t):
+            layer.block_bwd(tp.TP_ATTN, r, X, layer.dH, layer.partials[r])
+        e[7].record()
+        layer.reduce(layer.dX, None, layer.dH)
+        e[8].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = [[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(8)] for k in range(steps)]
+    return seg, wall
+
+
+def cpu_baseline(cfg, target_s=15.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the same
+    workload: rank 0's share of the layer, forward + backward of both blocks,
+    over the first L tokens of each sequence; FLOPs by the same formula."""
+    import numpy as np
+    from megatron_tensor_layer_amd import inputs as I
+    from oracle import tp_layer_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    parts = I.params_rank(cfg, 0)
+    pr = {k: v.astype(np.float64) for k, v in parts.items()}
+    ar = cfg.a // cfg.t
+
+    def run(L):
+        T = L * cfg.b
+        X = I.activation(cfg, "X", tokens=T).astype(np.float64)
+        dY = I.activation(cfg, "dY", tokens=T).astype(np.float64)
+        t0 = time.perf_counter()
+        pa, ca = O.attention_rank_forward(X, pr, L, cfg.b, ar)
+        H = O.block_output([pa], pr["bo"], X)
+        pm, cm = O.mlp_rank_forward(H, pr)
+        gm = O.mlp_rank_backward(cm, pr, dY)
+        dH = O.block_output([gm["dH"]], residual=dY)
+        O.attention_rank_backward(ca, pr, dH, L, cfg.b, ar)
+        return time.perf_counter() - t0
+
+    L = 64
+    el = run(L)
+    while el < target_s / 3 and L * 2 <= cfg.s:
+        L *= 2
+        el = run(L)
+    flops = model_flops_per_rank(cfg.h, L, cfg.b, cfg.t)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(el, 3),
+            "sample": f"rank 0 of t={cfg.t}, fwd+bwd of both blocks, first {L} of {cfg.s} tokens x b={cfg.b} "
+                      f"(numpy float64, {threads} BLAS threads); FLOPs = 72 b L h^2 (1 + L/6h) / t"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the t tensor-parallel ranks "
+              "run one after another on a single MI355X and no collectives run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from megatron_tensor_layer_amd import inputs as I
+    from megatron_tensor_layer_amd import tplayer as tp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tp.lib()
+    cfg = I.CONFIGS[args.config]
+    h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    layer, X, dY = build_layer(cfg)
+    for _ in range(args.warmup):
+        layer.forward(X)
+        layer.backward(dY)
+    torch.cuda.synchronize()
+
+    seg, wall = timed_steps(layer, X, dY, args.steps)
+    seg = np.array(seg)
+    rank_loops = seg[:, [0, 2, 4, 6]].sum(axis=1)          # ms per step, all t ranks
+    standin = seg[:, [1, 3, 5, 7]].sum(axis=1)
+    step_ms = seg.sum(axis=1)
+    t_rank = float(np.mean(rank_loops)) / t
+    F_rank = model_flops_per_rank(h, s, b, t)
+    tflops = F_rank / (t_rank * 1e-3) / 1e12
+
+    # per-role kernel times from the library's event profiler, one extra step
+    tp.tp_prof_enable(True)
+    layer.forward(X)
+    layer.backward(dY)
+    tp.tp_prof_enable(False)
+    prof = tp.tp_prof_read()
+    roles = {}
+    for name, e in prof.items():
+        roles[name] = {"launches": e["launches"], "ms_per_launch": round(e["ms"] / e["launches"], 4),
+                       "tflops": round(e["flops"] / (e["ms"] * 1e-3) / 1e12, 1) if e["ms"] > 0 else None,
+                       "gbps": round(e["bytes"] / (e["ms"] * 1e-3) / 1e9, 1) if e["ms"] > 0 else None}
+    gemm_roles = {k: v for k, v in prof.items() if k not in ("softmax", "rowdot", "reduce", "db1", "db2", "dbo",
+                                                              "dbqkv")}
+    dom = max(gemm_roles, key=lambda k: gemm_roles[k]["ms"])
+    de = prof[dom]
+    per_launch_ms = de["ms"] / de["launches"]
+    achieved = de["flops"] / de["launches"] / (per_launch_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": f"gemm_kernel role {dom}", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "flops_per_launch": de["flops"] / de["launches"],
+                "ms_per_launch": round(per_launch_ms, 4)}
+
+    out = {
+        "metric": "model TFLOP/s per GPU (layer fwd+bwd, one TP shard) and % of bf16 MFMA peak",
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(step_ms)), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) weights/biases, N(0,1) X and dY, drawn on the GPU)",
+        "config": {"workload": f"{cfg.name} layer shard: h={h}, a={a}, s={s}, b={b}, t={t}, fwd+bwd, causal",
+                   "h": h, "a": a, "s": s, "b": b, "t": t, "global_batch": b, "seq_len": s,
+                   "parallelism": f"tp{t} ranks run sequentially on one GPU"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "rank_ms": round(t_rank, 4),
+        "rank_ms_min": round(float(np.min(rank_loops)) / t, 4),
+        "standin_reduce_ms_per_step": round(float(np.mean(standin)), 4),
+        "flops_per_rank": F_rank,
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "roles": roles,
+        "context": "pages: 163 TFLOP/s per A100 (52% of 312) end-to-end with recompute; not this metric",
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -123,20 +123,22 @@ __global__ void __launch_bounds__(256) causal_softmax_long_kernel(const float* _
 // Equals rowsum(P * dP) of the softmax backward because C = P V.
 // One thread per (token row, head).
 // ---------------------------------------------------------------------------
+// C is read in fp32 (the unrounded P V accumulator), so D matches the row
+// sums of P * dP that the dS epilogue subtracts it from.
 template <typename T>
-__global__ void __launch_bounds__(256) rowdot_kernel(const T* __restrict__ dC, const T* __restrict__ C,
+__global__ void __launch_bounds__(256) rowdot_kernel(const T* __restrict__ dC, const float* __restrict__ C,
                                                      float* __restrict__ D, int Trows, int b, int ar, int d, int s) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)Trows * ar) return;
   const int row = (int)(idx / ar), j = (int)(idx - (idx / ar) * ar);
   const long ld = (long)ar * d;
   const T* x = dC + row * ld + (long)j * d;
-  const T* y = C + row * ld + (long)j * d;
+  const float* y = C + row * ld + (long)j * d;
   float acc = 0.0f;
   for (int c = 0; c < d; c += 4) {
     float u[4], v[4];
     Elt<T>::load4(x + c, u);
-    Elt<T>::load4(y + c, v);
+    Elt<float>::load4(y + c, v);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc += u[e] * v[e];
   }

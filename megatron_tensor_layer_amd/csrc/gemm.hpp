@@ -41,7 +41,10 @@ enum EpiKind : int {
   EPI_BIAS_GELU = 1,    // U = acc + bias[n] -> C;  GELU(U) -> C2
   EPI_GELU_BWD = 2,     // C = acc * gelu'(aux[m,n])
   EPI_SOFTMAX_BWD = 3,  // C = (n <= m) ? alpha * aux[m,n] * (acc - rowv[m]) : 0
-  EPI_PARTIAL = 4       // split-K: fp32 partial[split, m, n] = acc
+  EPI_PARTIAL = 4,      // split-K: fp32 partial[split, m, n] = acc
+  EPI_BIAS_SPLIT = 5,   // V = acc + bias[n] -> C (bf16); for n < c2_cols also the
+                        // rounding residual V - bf16(V) -> C2 (bf16), same layout
+  EPI_DUAL_F32 = 6      // C = acc (storage type) and C2 = acc (fp32), same layout
 };
 
 enum KMode : int {
@@ -58,8 +61,12 @@ struct GemmArgs {
   int kmode;
   int splits, k_chunk;   // split-K (EPI_PARTIAL pass)
   int group_m;           // tile-rows per ordering group
+  int kseg, kseg_len;    // kseg = 3: K runs over (A,B), (A,B2), (A2,B), each kseg_len long
+  int c2_cols;           // EPI_BIAS_SPLIT: columns that get a residual in C2
   const void* A; long lda, a_s1, a_s2;
   const void* B; long ldb, b_s1, b_s2;
+  const void* A2;  // second halves of split operands: same strides as A / B
+  const void* B2;
   void* C; long ldc, c_s1, c_s2;
   void* C2; long ldc2;
   const void* bias;
@@ -251,6 +258,19 @@ __device__ __forceinline__ void epi_apply(const GemmArgs& p, int z1, int z2, int
       Elt<T>::load4(static_cast<const T*>(p.aux) + (long)row * p.ldx + col, u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+    } else if constexpr (EPI == EPI_BIAS_SPLIT) {
+      float bb[4];
+      Elt<T>::load4(static_cast<const T*>(p.bias) + col, bb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += bb[e];
+      if (col < p.c2_cols) {
+        float lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
+        Elt<T>::store4(static_cast<T*>(p.C2) + (long)row * p.ldc + col, lo);
+      }
+    } else if constexpr (EPI == EPI_DUAL_F32) {
+      Elt<float>::store4(static_cast<float*>(p.C2) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
     } else if constexpr (EPI == EPI_SOFTMAX_BWD) {
       float pp[4];
       Elt<T>::load4(static_cast<const T*>(p.aux) + z1 * p.x_s1 + z2 * p.x_s2 + (long)row * p.ldx + col, pp);
@@ -317,7 +337,25 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(const GemmArgs p) {
     kb = blockIdx.y * p.k_chunk;
     ke = min(ke, kb + p.k_chunk);
   }
-  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+  // K tiles: one run [kb, ke), or kseg runs of kseg_len over operand pairs
+  const int nkd = p.kseg > 1 ? (p.kseg_len + BK - 1) / BK : 0;
+  const int nk = p.kseg > 1 ? p.kseg * nkd : (ke > kb ? (ke - kb + BK - 1) / BK : 0);
+  const T* A2 = p.kseg > 1 ? static_cast<const T*>(p.A2) + z1 * p.a_s1 + z2 * p.a_s2 : A;
+  const T* B2 = p.kseg > 1 ? static_cast<const T*>(p.B2) + z1 * p.b_s1 + z2 * p.b_s2 : B;
+  auto tile_src = [&](int kt, const T*& a, const T*& b, int& k0, int& kend) {
+    if (p.kseg > 1) {
+      const int seg = kt / nkd;
+      k0 = (kt - seg * nkd) * BK;
+      kend = p.kseg_len;
+      a = seg == 2 ? A2 : A;
+      b = seg == 1 ? B2 : B;
+    } else {
+      k0 = kb + kt * BK;
+      kend = ke;
+      a = A;
+      b = B;
+    }
+  };
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -331,8 +369,11 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(const GemmArgs p) {
   typename LoaderSel<BKM, T, BN, NT>::type lb;
 
   if (nk > 0) {
-    la.load(A, p.lda, m0, p.M, kb, ke, tid);
-    lb.load(B, p.ldb, n0, p.N, kb, ke, tid);
+    const T *a, *b;
+    int k0, kend;
+    tile_src(0, a, b, k0, kend);
+    la.load(a, p.lda, m0, p.M, k0, kend, tid);
+    lb.load(b, p.ldb, n0, p.N, k0, kend, tid);
     la.store(smem, tid);
     lb.store(smem + BM * 8, tid);
   }
@@ -344,9 +385,11 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(const GemmArgs p) {
     const uint4* Bs = As + BM * 8;
     const bool more = kt + 1 < nk;
     if (more) {
-      const int kn = kb + (kt + 1) * BK;
-      la.load(A, p.lda, m0, p.M, kn, ke, tid);
-      lb.load(B, p.ldb, n0, p.N, kn, ke, tid);
+      const T *a, *b;
+      int k0, kend;
+      tile_src(kt + 1, a, b, k0, kend);
+      la.load(a, p.lda, m0, p.M, k0, kend, tid);
+      lb.load(b, p.ldb, n0, p.N, k0, kend, tid);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {

@@ -170,8 +170,10 @@ int choose_splits(long M, long N, long K) {
 // of the attention tile in every row; all causal GEMMs use this tile.
 int att_tile(int dt) { return dt == TP_BF16 ? CfgMid::BM : CfgF32::BM; }
 
+// ATTN keeps QKV, P and C (and, for bf16, C in fp32 for the softmax
+// backward's row term); MLP keeps U and Z.
 struct SavedLayout {
-  size_t qkv, p, c, u, z, total;
+  size_t qkv, p, c, c32, u, z, total;
 };
 SavedLayout saved_layout(const Dims& D, int blk) {
   SavedLayout L{};
@@ -180,6 +182,11 @@ SavedLayout saved_layout(const Dims& D, int blk) {
     L.qkv = o; o = al(o + (size_t)D.T * D.q3 * D.es);
     L.p = o;   o = al(o + (size_t)D.z * D.s * D.s * D.es);
     L.c = o;   o = al(o + (size_t)D.T * D.hr * D.es);
+    if (D.dt == TP_BF16) {
+      L.c32 = o; o = al(o + (size_t)D.T * D.hr * 4);
+    } else {
+      L.c32 = L.c;
+    }
   } else {
     L.u = o; o = al(o + (size_t)D.T * D.fr * D.es);
     L.z = o; o = al(o + (size_t)D.T * D.fr * D.es);
@@ -195,7 +202,7 @@ size_t partial_bytes(const Dims& D, long M, long N, long K) {
 }
 
 struct WsLayout {
-  size_t s;                 // attn fwd: fp32 scores
+  size_t s, qkv_lo;         // attn fwd: fp32 scores, bf16 residuals of Q and K
   size_t dc, D, ds, dqkv;   // attn bwd
   size_t du;                // mlp bwd
   size_t part, part_bytes;  // split-K partials
@@ -208,7 +215,9 @@ WsLayout ws_layout(const Dims& D, int blk) {
   if (blk == TP_ATTN) {
     upd(D.T, D.q3, D.h); upd(D.T, D.h, D.hr);
     upd(D.T, D.hr, D.h); upd(D.hr, D.h, D.T); upd(D.T, D.h, D.q3); upd(D.h, D.q3, D.T);
-    const size_t fwd = al((size_t)D.z * D.s * D.s * 4);
+    size_t fwd = al((size_t)D.z * D.s * D.s * 4);
+    W.qkv_lo = fwd;
+    if (D.dt == TP_BF16) fwd = al(fwd + (size_t)D.T * D.q3 * D.es);
     size_t o = 0;
     W.dc = o;   o = al(o + (size_t)D.T * D.hr * D.es);
     W.D = o;    o = al(o + (size_t)D.z * D.s * 4);
@@ -261,8 +270,12 @@ hipError_t launch(GemmArgs p, int batch, hipStream_t st) {
 template <bool AK, bool BKM, int EPI, int ROLE, int KIND, bool OUTF32 = false>
 hipError_t run(const Dims& D, GemmArgs p, int batch, hipStream_t st) {
   if (D.dt == TP_FP32) {
-    p.splits = 1;
-    return launch<CfgF32, AK, BKM, EPI, float, 0>(p, batch, st);
+    if constexpr (EPI == EPI_BIAS_SPLIT || EPI == EPI_DUAL_F32) {
+      return hipErrorInvalidValue;  // bf16-only epilogues
+    } else {
+      p.splits = 1;
+      return launch<CfgF32, AK, BKM, EPI, float, 0>(p, batch, st);
+    }
   }
   if constexpr (KIND == KIND_BIG) {
     return launch<CfgBig, AK, BKM, EPI, bf16_t, ROLE>(p, batch, st);
@@ -320,9 +333,9 @@ hipError_t softmax_t(const Dims& D, const float* S, void* P, hipStream_t st) {
 }
 
 template <typename T>
-hipError_t rowdot_t(const Dims& D, const void* dC, const void* C, float* Dv, hipStream_t st) {
+hipError_t rowdot_t(const Dims& D, const void* dC, const float* C, float* Dv, hipStream_t st) {
   const long n = D.T * D.ar;
-  hipLaunchKernelGGL(rowdot_kernel<T>, dim3((unsigned)cdivl(n, 256)), dim3(256), 0, st, (const T*)dC, (const T*)C, Dv,
+  hipLaunchKernelGGL(rowdot_kernel<T>, dim3((unsigned)cdivl(n, 256)), dim3(256), 0, st, (const T*)dC, C, Dv,
                      (int)D.T, (int)D.b, (int)D.ar, (int)D.d, (int)D.s);
   return hipGetLastError();
 }
@@ -355,20 +368,31 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
   void* qkv = B8(saved, S.qkv);
   void* P = B8(saved, S.p);
   void* C = B8(saved, S.c);
+  void* C32 = B8(saved, S.c32);
   float* scores = reinterpret_cast<float*>(B8(ws, W.s));
+  void* qkv_lo = B8(ws, W.qkv_lo);
   float* part = reinterpret_cast<float*>(B8(ws, W.part));
   const double es = (double)D.es, sde = (double)D.z * D.s * D.d * es;
+  const bool bf = D.dt == TP_BF16;
 
-  {  // QKV_r = X Wqkv_r + b_qkv_r
+  {  // QKV_r = X Wqkv_r + b_qkv_r; bf16 also keeps the rounding residual of Q and K
     GemmArgs p = gargs(D.T, D.q3, D.h);
     p.A = x; p.lda = D.h;
     p.B = w->w_in; p.ldb = D.q3;
     p.C = qkv; p.ldc = D.q3;
     p.bias = w->b_in;
-    TRY((linear<true, false, EPI_LINEAR, R_QKV_FWD>(D, p, part, st)));
+    if (bf) {
+      p.C2 = qkv_lo; p.c2_cols = (int)(2 * D.hr);
+      TRY((linear<true, false, EPI_BIAS_SPLIT, R_QKV_FWD>(D, p, part, st)));
+    } else {
+      TRY((linear<true, false, EPI_LINEAR, R_QKV_FWD>(D, p, part, st)));
+    }
   }
-  {  // S_z = Q_z K_z^T / sqrt(d), lower-triangular tiles, fp32
-    prof::Scope sc(R_SCORES, att_flops(D), 2 * sde + 4.0 * tri_elems(D), st);
+  {  // S_z = Q_z K_z^T / sqrt(d), lower-triangular tiles, fp32.
+     // bf16: Q = Qh + Ql, K = Kh + Kl (Ql, Kl the bf16 rounding residuals);
+     // S = Qh Kh^T + Qh Kl^T + Ql Kh^T in one K-segmented MFMA pass, which
+     // keeps the logits of peaked softmax rows accurate to about 2^-16.
+    prof::Scope sc(R_SCORES, att_flops(D), (bf ? 4 : 2) * sde + 4.0 * tri_elems(D), st);
     GemmArgs p = gargs(D.s, D.s, D.d);
     p.zdiv = (int)D.ar;
     p.A = qkv; p.lda = D.b * D.q3; p.a_s1 = D.q3; p.a_s2 = D.d;
@@ -376,6 +400,11 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
     p.C = scores; p.ldc = D.s; p.c_s1 = D.ar * D.s * D.s; p.c_s2 = D.s * D.s;
     p.alpha = (float)(1.0 / std::sqrt((double)D.d));
     p.tri = 1;
+    if (bf) {
+      p.A2 = qkv_lo;
+      p.B2 = B8(qkv_lo, (size_t)D.hr * D.es);
+      p.kseg = 3; p.kseg_len = (int)D.d;
+    }
     TRY((run<true, true, EPI_LINEAR, R_SCORES, KIND_MID, true>(D, p, (int)D.z, st)));
   }
   {  // P = causal softmax(S)
@@ -391,7 +420,12 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
     p.B = B8(qkv, (size_t)2 * D.hr * D.es); p.ldb = D.b * D.q3; p.b_s1 = D.q3; p.b_s2 = D.d;
     p.C = C; p.ldc = D.b * D.hr; p.c_s1 = D.hr; p.c_s2 = D.d;
     p.kmode = K_LOWER;
-    TRY((run<true, false, EPI_LINEAR, R_PV, KIND_MID>(D, p, (int)D.z, st)));
+    if (bf) {
+      p.C2 = C32;
+      TRY((run<true, false, EPI_DUAL_F32, R_PV, KIND_MID>(D, p, (int)D.z, st)));
+    } else {
+      TRY((run<true, false, EPI_LINEAR, R_PV, KIND_MID>(D, p, (int)D.z, st)));
+    }
   }
   {  // partial = C Wo_r
     GemmArgs p = gargs(D.T, D.h, D.hr);
@@ -410,6 +444,7 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
   const void* qkv = B8(saved, S.qkv);
   const void* P = B8(saved, S.p);
   const void* C = B8(saved, S.c);
+  const float* C32 = reinterpret_cast<const float*>(B8(saved, S.c32));
   void* dC = B8(ws, W.dc);
   float* Dv = reinterpret_cast<float*>(B8(ws, W.D));
   void* dS = B8(ws, W.ds);
@@ -434,9 +469,9 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
   }
   TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, st));  // dbo (replica)
   {  // D = rowsum(dC * C) per (sequence, head, query)
-    prof::Scope sc(R_ROWDOT, 2.0 * D.T * D.hr, 2.0 * D.T * D.hr * es + 4.0 * D.z * D.s, st);
-    if (D.dt == TP_BF16) TRY(rowdot_t<bf16_t>(D, dC, C, Dv, st));
-    else TRY(rowdot_t<float>(D, dC, C, Dv, st));
+    prof::Scope sc(R_ROWDOT, 2.0 * D.T * D.hr, D.T * D.hr * (es + 4.0) + 4.0 * D.z * D.s, st);
+    if (D.dt == TP_BF16) TRY(rowdot_t<bf16_t>(D, dC, C32, Dv, st));
+    else TRY(rowdot_t<float>(D, dC, C32, Dv, st));
   }
   {  // dS = P * (dC V^T - D) / sqrt(d), lower-triangular tiles
     prof::Scope sc(R_DS, att_flops(D), 2 * sde + 2 * es * tri_elems(D) + 4.0 * D.z * D.s, st);
