@@ -92,38 +92,60 @@ struct TileCfg {
 
 // ---------------------------------------------------------------------------
 // global -> LDS loaders
+//
+// Each thread owns fixed 16-byte chunks of the BM x BK (BN x BK) tile; their
+// element offsets relative to the tile's k origin are computed once. Rows
+// beyond M (N) are clamped to the last valid row: they only feed output rows
+// (columns) that are never stored. k beyond the K range must read as zero;
+// that happens only in a ragged last K tile, handled by a uniform branch.
 // ---------------------------------------------------------------------------
 
 // Operand stored K-contiguous: element (row, k) at base[row*ld + k].
 template <typename T, int R, int NT>
 struct KLoader {
   static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int BK = 8 * VEC;
   static constexpr int TOTAL = R * 8;  // 16-byte chunks in an R x BK tile
-  static constexpr int CH = (TOTAL + NT - 1) / NT;
+  static_assert(TOTAL % NT == 0, "tile rows must cover the threads");
+  static constexpr int CH = TOTAL / NT;
+  static constexpr int LOADS = CH, STORES = CH;  // global loads / LDS stores per tile
+  uint32_t off[CH];
   uint4 v[CH];
 
-  __device__ __forceinline__ void load(const T* base, long ld, int row0, int rlim, int k0, int ke, int tid) {
+  __device__ __forceinline__ void init(long ld, int row0, int rlim, int tid) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + i * NT;
-      const int r = c >> 3, kc = c & 7;
-      const int row = row0 + r, k = k0 + kc * VEC;
-      const bool ok = (TOTAL % NT == 0 || c < TOTAL) && row < rlim && k < ke;
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) x = *reinterpret_cast<const uint4*>(base + (long)row * ld + k);
-      v[i] = x;
+      const int row = min(row0 + (c >> 3), rlim - 1);
+      off[i] = (uint32_t)((long)row * ld + (c & 7) * VEC);
+    }
+  }
+  // base = operand origin advanced to the tile's first k; kvalid = k range
+  // left (> 0). TAIL: chunks at k >= kvalid read the tile's first chunk of the
+  // row (always in bounds) and are replaced by zeros.
+  template <bool TAIL>
+  __device__ __forceinline__ void load(const T* base, long ld, int kvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if constexpr (!TAIL) {
+        v[i] = *reinterpret_cast<const uint4*>(base + off[i]);
+      } else {
+        const int kc = ((tid + i * NT) & 7) * VEC;
+        const bool ok = kc < kvalid;
+        const uint4 x = *reinterpret_cast<const uint4*>(base + (off[i] - (ok ? 0 : kc)));
+        v[i] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   }
   __device__ __forceinline__ void store(uint4* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + i * NT;
-      if (TOTAL % NT == 0 || c < TOTAL) {
-        const int r = c >> 3, kc = c & 7;
-        lds[r * 8 + (kc ^ (r & 7))] = v[i];
-      }
+      const int r = c >> 3, kc = c & 7;
+      lds[r * 8 + (kc ^ (r & 7))] = v[i];
     }
   }
+  __device__ __forceinline__ static const T* advance(const T* base, long ld, int k) { return base + k; }
 };
 
 __device__ __forceinline__ uint32_t dw(const uint4& x, int q) {
@@ -138,7 +160,7 @@ __device__ __forceinline__ void transpose_blk(const uint4 (&in)[8], uint4 (&out)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t lo = dw(in[2 * q], j >> 1), hi = dw(in[2 * q + 1], j >> 1);
-      w[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      w[q] = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u) : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
     out[j] = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -150,27 +172,42 @@ __device__ __forceinline__ void transpose_blk(const uint4 (&in)[4], uint4 (&out)
   for (int j = 0; j < 4; ++j) out[j] = make_uint4(dw(in[0], j), dw(in[1], j), dw(in[2], j), dw(in[3], j));
 }
 
-// Operand stored M/N-contiguous: element (mn, k) at base[k*ld + mn].
+// Operand stored M/N-contiguous: element (mn, k) at base[k*ld + mn]. A thread
+// loads VEC rows of k x 16 bytes of mn and transposes them in registers.
 template <typename T, int R, int NT>
 struct MNLoader {
   static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int BK = 8 * VEC;
   static constexpr int TOTAL = (R / VEC) * 8;  // VEC x VEC blocks in an R x BK tile
   static constexpr int BPT = (TOTAL + NT - 1) / NT;
+  static constexpr int LOADS = BPT * VEC, STORES = BPT * VEC;
+  uint32_t off[BPT];
   uint4 v[BPT][VEC];
 
-  __device__ __forceinline__ void load(const T* base, long ld, int mn0, int mnlim, int k0, int ke, int tid) {
+  __device__ __forceinline__ void init(long ld, int mn0, int mnlim, int tid) {
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-      const int c = tid + b * NT;
-      const int kc = c & 7, mb = c >> 3;
-      const int mn = mn0 + mb * VEC;
-      const bool okb = (TOTAL % NT == 0 || c < TOTAL) && mn < mnlim;
+      const int c = min(tid + b * NT, TOTAL - 1);
+      const int kc = c & 7;
+      const int mn = min(mn0 + (c >> 3) * VEC, mnlim - VEC);
+      off[b] = (uint32_t)((long)(kc * VEC) * ld + mn);
+    }
+  }
+  template <bool TAIL>
+  __device__ __forceinline__ void load(const T* base, long ld, int kvalid, int tid) {
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      const int kc = (min(tid + b * NT, TOTAL - 1) & 7) * VEC;
 #pragma unroll
       for (int r = 0; r < VEC; ++r) {
-        const int k = k0 + kc * VEC + r;
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (okb && k < ke) x = *reinterpret_cast<const uint4*>(base + (long)k * ld + mn);
-        v[b][r] = x;
+        if constexpr (!TAIL) {
+          v[b][r] = *reinterpret_cast<const uint4*>(base + r * ld + off[b]);
+        } else {
+          // rows k >= kvalid read row 0 of the tile (in bounds) and become zeros
+          const bool ok = kc + r < kvalid;
+          const uint4 x = *reinterpret_cast<const uint4*>(base + (ok ? r * ld + off[b] : off[b] - (long)kc * ld));
+          v[b][r] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
   }
@@ -190,6 +227,7 @@ struct MNLoader {
       }
     }
   }
+  __device__ __forceinline__ static const T* advance(const T* base, long ld, int k) { return base + (long)k * ld; }
 };
 
 template <bool KMAJ, typename T, int R, int NT>
@@ -283,6 +321,31 @@ __device__ __forceinline__ void epi_apply(const GemmArgs& p, int z1, int z2, int
 }
 
 // ---------------------------------------------------------------------------
+// instruction interleaving hints (sched_group_barrier masks: 0x008 MFMA,
+// 0x020 global read, 0x100 LDS read, 0x200 LDS write)
+// ---------------------------------------------------------------------------
+
+template <int N, int MASK>
+__device__ __forceinline__ void sched_pairs() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(MASK, 1, 0);
+    sched_pairs<N - 1, MASK>();
+  }
+}
+
+// One sub-step of MF MFMAs: RD fragment reads, then OT ops of kind OMASK,
+// each paired with one MFMA; the remaining MFMAs back to back.
+template <int MF, int RD, int OT, int OMASK>
+__device__ __forceinline__ void sched_substep() {
+  constexpr int r = RD < MF ? RD : MF;
+  constexpr int o = OT < MF - r ? OT : MF - r;
+  sched_pairs<r, 0x100>();
+  sched_pairs<o, OMASK>();
+  if constexpr (MF - r - o > 0) __builtin_amdgcn_sched_group_barrier(0x008, MF - r - o, 0);
+}
+
+// ---------------------------------------------------------------------------
 // tile scheduling
 // ---------------------------------------------------------------------------
 
@@ -313,8 +376,10 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn)
 
 // ROLE only names the instantiation (one kernel symbol per GEMM of the layer,
 // so profilers attribute time per GEMM); it does not change the code.
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE>
-__global__ void __launch_bounds__(Cfg::NT) gemm_kernel(const GemmArgs p) {
+// KSEG = 3 runs the K loop over (A, B), (A, B2) and (A2, B) in turn.
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool TAIL = false,
+          bool SCHED = true>
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) gemm_kernel(const GemmArgs p) {
   using T = typename Cfg::T;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BK = Cfg::BK;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;
@@ -327,33 +392,44 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(const GemmArgs p) {
   tile_coords(p, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int z = blockIdx.z, z1 = z / p.zdiv, z2 = z - (z / p.zdiv) * p.zdiv;
-  const T* A = static_cast<const T*>(p.A) + z1 * p.a_s1 + z2 * p.a_s2;
-  const T* B = static_cast<const T*>(p.B) + z1 * p.b_s1 + z2 * p.b_s2;
+  const long aoff = z1 * p.a_s1 + z2 * p.a_s2, boff = z1 * p.b_s1 + z2 * p.b_s2;
+  const T* A = static_cast<const T*>(p.A) + aoff;
+  const T* B = static_cast<const T*>(p.B) + boff;
 
-  int kb = 0, ke = p.K;
-  if (p.kmode == K_LOWER) ke = min(ke, m0 + BM);
-  else if (p.kmode == K_UPPER) kb = m0;
-  if constexpr (EPI == EPI_PARTIAL) {
-    kb = blockIdx.y * p.k_chunk;
-    ke = min(ke, kb + p.k_chunk);
+  using LA = typename LoaderSel<AK, T, BM, NT>::type;
+  using LB = typename LoaderSel<BKM, T, BN, NT>::type;
+  LA la;
+  LB lb;
+  la.init(p.lda, m0, p.M, tid);
+  lb.init(p.ldb, n0, p.N, tid);
+
+  // K tiles: one run [kb, ke), or KSEG runs of kseg_len over operand pairs
+  int kb = 0, ke = p.K, nk, nkd = 1;
+  if constexpr (KSEG > 1) {
+    nkd = (p.kseg_len + BK - 1) / BK;
+    nk = KSEG * nkd;
+  } else {
+    if (p.kmode == K_LOWER) ke = min(ke, m0 + BM);
+    else if (p.kmode == K_UPPER) kb = m0;
+    if constexpr (EPI == EPI_PARTIAL) {
+      kb = blockIdx.y * p.k_chunk;
+      ke = min(ke, kb + p.k_chunk);
+    }
+    nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
   }
-  // K tiles: one run [kb, ke), or kseg runs of kseg_len over operand pairs
-  const int nkd = p.kseg > 1 ? (p.kseg_len + BK - 1) / BK : 0;
-  const int nk = p.kseg > 1 ? p.kseg * nkd : (ke > kb ? (ke - kb + BK - 1) / BK : 0);
-  const T* A2 = p.kseg > 1 ? static_cast<const T*>(p.A2) + z1 * p.a_s1 + z2 * p.a_s2 : A;
-  const T* B2 = p.kseg > 1 ? static_cast<const T*>(p.B2) + z1 * p.b_s1 + z2 * p.b_s2 : B;
-  auto tile_src = [&](int kt, const T*& a, const T*& b, int& k0, int& kend) {
-    if (p.kseg > 1) {
+  // operand origins of K tile kt and the k range left in its run
+  auto src = [&](int kt, const T*& a, const T*& b, int& kvalid) {
+    if constexpr (KSEG > 1) {
       const int seg = kt / nkd;
-      k0 = (kt - seg * nkd) * BK;
-      kend = p.kseg_len;
-      a = seg == 2 ? A2 : A;
-      b = seg == 1 ? B2 : B;
+      const int k0 = (kt - seg * nkd) * BK;
+      kvalid = p.kseg_len - k0;
+      a = LA::advance(seg == 2 ? static_cast<const T*>(p.A2) + aoff : A, p.lda, k0);
+      b = LB::advance(seg == 1 ? static_cast<const T*>(p.B2) + boff : B, p.ldb, k0);
     } else {
-      k0 = kb + kt * BK;
-      kend = ke;
-      a = A;
-      b = B;
+      const int k0 = kb + kt * BK;
+      kvalid = ke - k0;
+      a = LA::advance(A, p.lda, k0);
+      b = LB::advance(B, p.ldb, k0);
     }
   };
 
@@ -365,49 +441,77 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(const GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  typename LoaderSel<AK, T, BM, NT>::type la;
-  typename LoaderSel<BKM, T, BN, NT>::type lb;
-
+  // Pipeline: while the MFMAs of tile kt run from LDS buffer kt&1, tile kt+1
+  // (already in registers) is written to the other buffer and tile kt+2 is
+  // fetched from global memory into the registers. Past the last tile the
+  // fetches repeat the last tile (in bounds) and the stores go to the idle
+  // buffer, so the loop body is one branch-free block. One barrier per tile.
+  const int r32 = lane & 31, g = lane >> 5;
+  const int arow = (wm * WTM + r32) * 8, brow = (wn * WTN + r32) * 8;
   if (nk > 0) {
     const T *a, *b;
-    int k0, kend;
-    tile_src(0, a, b, k0, kend);
-    la.load(a, p.lda, m0, p.M, k0, kend, tid);
-    lb.load(b, p.ldb, n0, p.N, k0, kend, tid);
+    int kv;
+    src(0, a, b, kv);
+    la.template load<TAIL>(a, p.lda, kv, tid);
+    lb.template load<TAIL>(b, p.ldb, kv, tid);
     la.store(smem, tid);
     lb.store(smem + BM * 8, tid);
+    src(min(1, nk - 1), a, b, kv);
+    la.template load<TAIL>(a, p.lda, kv, tid);
+    lb.template load<TAIL>(b, p.ldb, kv, tid);
   }
   __syncthreads();
 
-  const int r32 = lane & 31, g = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const uint4* As = smem + (kt & 1) * (BM + BN) * 8;
     const uint4* Bs = As + BM * 8;
-    const bool more = kt + 1 < nk;
-    if (more) {
+    uint4* An = smem + ((kt + 1) & 1) * (BM + BN) * 8;
+    uint4 af[2][TM], bq[2][TN];
+    {
+      const int ch = g ^ (r32 & 7);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = As[arow + i * 32 * 8 + ch];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bq[0][j] = Bs[brow + j * 32 * 8 + ch];
+    }
+    la.store(An, tid);
+    lb.store(An + BM * 8, tid);
+    {
       const T *a, *b;
-      int k0, kend;
-      tile_src(kt + 1, a, b, k0, kend);
-      la.load(a, p.lda, m0, p.M, k0, kend, tid);
-      lb.load(b, p.ldb, n0, p.N, k0, kend, tid);
+      int kv;
+      src(min(kt + 2, nk - 1), a, b, kv);
+      la.template load<TAIL>(a, p.lda, kv, tid);
+      lb.template load<TAIL>(b, p.ldb, kv, tid);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int ch = (2 * ks + g) ^ (r32 & 7);
-      uint4 af[TM], bq[TN];
+      const int cur = ks & 1;
+      if (ks + 1 < 4) {
+        const int ch = (2 * (ks + 1) + g) ^ (r32 & 7);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = As[(wm * WTM + i * 32 + r32) * 8 + ch];
+        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = As[arow + i * 32 * 8 + ch];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bq[j] = Bs[(wn * WTN + j * 32 + r32) * 8 + ch];
+        for (int j = 0; j < TN; ++j) bq[cur ^ 1][j] = Bs[brow + j * 32 * 8 + ch];
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) mma16(bq[j], af[i], acc[i][j], T{});
+        for (int j = 0; j < TN; ++j) mma16(bq[cur][j], af[cur][i], acc[i][j], T{});
     }
-    if (more) {
-      uint4* An = smem + ((kt + 1) & 1) * (BM + BN) * 8;
-      la.store(An, tid);
-      lb.store(An + BM * 8, tid);
+    if constexpr (SCHED && LA::TOTAL % NT == 0 && LB::TOTAL % NT == 0) {
+      // Interleave, one LDS or global op per MFMA: sub-step 0's fragment
+      // reads first; in every sub-step the next sub-step's fragment reads;
+      // the stores of tile kt+1 in sub-steps 0-1, the global fetches of tile
+      // kt+2 (which reuse the store registers) in sub-steps 2-3.
+      constexpr int MF = TM * TN * (sizeof(T) == 2 ? 1 : 4);  // MFMAs per sub-step
+      constexpr int NRD = TM + TN;
+      constexpr int NWR = LA::STORES + LB::STORES;
+      constexpr int NLD = LA::LOADS + LB::LOADS;
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      sched_substep<MF, NRD, NWR / 2, 0x200>();
+      sched_substep<MF, NRD, NWR - NWR / 2, 0x200>();
+      sched_substep<MF, NRD, NLD / 2, 0x020>();
+      sched_substep<MF, 0, NLD - NLD / 2, 0x020>();
     }
     __syncthreads();
   }

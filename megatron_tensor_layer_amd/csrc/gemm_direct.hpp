@@ -1,0 +1,274 @@
+// bf16 MFMA GEMM for gfx950 with direct global -> LDS tile loads.
+//
+// Same contract as gemm_kernel (gemm.hpp): C = epilogue(op(A) op(B)), fp32
+// accumulation, one 256x256 (or 128x128) output tile per block of four waves.
+// The operand tiles travel from HBM straight into LDS with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at dst + 16 * lane), so
+// the K loop needs no staging registers and no LDS store instructions, and a
+// tile's loads have a whole K step of MFMA work to hide behind:
+//
+//   iteration kt:  issue loads of tile kt+1 into the idle LDS buffer
+//                  4 sub-steps x (fragment reads + MFMAs) on tile kt
+//                  wait for the loads, barrier
+//
+// LDS layouts (one 64-deep K tile):
+//  * K-contiguous operand: row = m (or n), 128 bytes = 64 k; the eight
+//    16-byte chunks of row r are stored at chunk ^ (r & 7). MFMA fragments
+//    (8 consecutive k of one row) are single ds_read_b128, conflict free.
+//  * M/N-contiguous operand: row = k, BM*2 (BN*2) bytes of m (n); the 32-byte
+//    segments of row k are stored at segment ^ (k & 3). Fragments come from
+//    two ds_read_b64_tr_b16 per lane: within each 16-lane group, lane i gets
+//    element i%4 of the 8-byte chunks addressed by lanes 4c + i/4 (c = 0..3),
+//    so addressing rows k = 4c' + ... and columns 16*(g%2) + 4*(i%4) hands
+//    every lane 4 consecutive k of one column; the XOR keeps the four rows
+//    of a group on distinct banks.
+// The swizzles are applied by choosing which global chunk each lane loads.
+// Rows (columns) beyond M (N) are clamped to the last valid one: they only
+// feed outputs that are never stored. K runs must be multiples of 64; ragged
+// K uses gemm_kernel.
+#pragma once
+
+#include "gemm.hpp"
+
+namespace tpl {
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+#define TPL_LDS __attribute__((address_space(3)))
+#define TPL_GLOBAL __attribute__((address_space(1)))
+
+// global_load_lds_dwordx4 with a wave-uniform base (SGPRs), a per-lane
+// 32-bit byte offset and the wave's LDS destination in M0. Issued as inline
+// assembly so that the compiler does not serialize the tile's LDS fragment
+// reads behind these loads (it cannot tell that they target the other
+// buffer); the kernel waits for them explicitly (vmcnt(0)) before each
+// barrier. Loads the compiler issues itself stay correctly ordered: extra
+// outstanding loads only make its own vmcnt waits more conservative.
+__device__ __forceinline__ const bf16_t* uniform_ptr(const bf16_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const bf16_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void load_lds16(const bf16_t* base, uint32_t byte_off, uint4* lds_dst) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(byte_off), "s"(uniform_ptr(base))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint2 read_tr(const uint4* lds, uint32_t byte_off) {
+  const TPL_LDS v4i16_t* p = (const TPL_LDS v4i16_t*)((const TPL_LDS char*)lds + byte_off);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPL_LDS v4i16_t*)p));
+}
+
+// One operand's tile loader + fragment reader. R = rows of the operand tile
+// along M (or N); KMAJ = operand stored K-contiguous in HBM.
+template <bool KMAJ, int R, int NT>
+struct DirectOperand {
+  static constexpr int BK = 64;
+  static constexpr int TILE_BYTES = R * BK * 2;
+  static constexpr int INSTS = TILE_BYTES / 1024;  // wave-wide 1 KB loads per tile
+  static constexpr int WAVES = NT / 64;
+  static_assert(INSTS % WAVES == 0, "tile must split evenly over the waves");
+  static constexpr int PER_WAVE = INSTS / WAVES;
+  static constexpr int ROW_UNITS = R / 8;  // 16-byte units per k-row (M/N-major)
+  uint32_t off[PER_WAVE];                  // element offsets at the tile's k origin
+
+  __device__ __forceinline__ void init(long ld, int mn0, int lim, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int inst = wave * PER_WAVE + i;
+      if constexpr (KMAJ) {
+        const int row = inst * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ (row & 7);
+        const int g = min(mn0 + row, lim - 1);
+        off[i] = (uint32_t)((long)g * ld + chunk * 8);
+      } else {
+        constexpr int ROWS_PER_INST = 64 / ROW_UNITS;
+        const int k = inst * ROWS_PER_INST + lane / ROW_UNITS;
+        const int unit = (lane % ROW_UNITS) ^ (2 * (k & 3));
+        const int col = min(mn0 + unit * 8, lim - 8);
+        off[i] = (uint32_t)((long)k * ld + col);
+      }
+    }
+  }
+  // base: operand origin advanced to the tile's first k
+  __device__ __forceinline__ void issue(const bf16_t* base, uint4* lds, int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) load_lds16(base, off[i] * 2u, lds + (wave * PER_WAVE + i) * 64);
+  }
+  __device__ __forceinline__ static const bf16_t* advance(const bf16_t* base, long ld, int k) {
+    return KMAJ ? base + k : base + (long)k * ld;
+  }
+  // Fragment for rows [r0, r0 + 32) and k [16 ks, 16 ks + 16): lane l gets
+  // row r0 + l % 32, k = 16 ks + 8 (l / 32) + (0..7).
+  __device__ __forceinline__ uint4 frag(const uint4* lds, int r0, int ks, int lane) const {
+    if constexpr (KMAJ) {
+      const int row = r0 + (lane & 31);
+      return lds[row * 8 + ((2 * ks + (lane >> 5)) ^ (row & 7))];
+    } else {
+      const int g = lane >> 4, i = lane & 15;
+      const int col = r0 + 16 * (g & 1) + 4 * (i & 3);
+      const int kb = 16 * ks + 8 * (g >> 1) + (i >> 2);
+      uint2 lo, hi;
+      {
+        const int k = kb;
+        lo = read_tr(lds, (uint32_t)(k * R * 2 + (((col >> 3) ^ (2 * (k & 3))) << 4) + 2 * (col & 7)));
+      }
+      {
+        const int k = kb + 4;
+        hi = read_tr(lds, (uint32_t)(k * R * 2 + (((col >> 3) ^ (2 * (k & 3))) << 4) + 2 * (col & 7)));
+      }
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+};
+
+#ifndef TPL_DIRECT_SCHED
+#define TPL_DIRECT_SCHED 0
+#endif
+
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED>
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_direct_kernel(const GemmArgs p) {
+  static_assert(sizeof(typename Cfg::T) == 2, "direct path is bf16");
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BK = 64;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;
+  using OA = DirectOperand<AK, BM, NT>;
+  using OB = DirectOperand<BKM, BN, NT>;
+  __shared__ __attribute__((aligned(1024))) uint4 sa0[BM * 8];
+  __shared__ __attribute__((aligned(1024))) uint4 sb0[BN * 8];
+  __shared__ __attribute__((aligned(1024))) uint4 sa1[BM * 8];
+  __shared__ __attribute__((aligned(1024))) uint4 sb1[BN * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Cfg::WN, wn = wave - (wave / Cfg::WN) * Cfg::WN;
+
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.z, z1 = z / p.zdiv, z2 = z - (z / p.zdiv) * p.zdiv;
+  const long aoff = z1 * p.a_s1 + z2 * p.a_s2, boff = z1 * p.b_s1 + z2 * p.b_s2;
+  const bf16_t* A = static_cast<const bf16_t*>(p.A) + aoff;
+  const bf16_t* B = static_cast<const bf16_t*>(p.B) + boff;
+
+  OA oa;
+  OB ob;
+  oa.init(p.lda, m0, p.M, wave, lane);
+  ob.init(p.ldb, n0, p.N, wave, lane);
+
+  int kb = 0, ke = p.K, nk, nkd = 1;
+  if constexpr (KSEG > 1) {
+    nkd = p.kseg_len / BK;
+    nk = KSEG * nkd;
+  } else {
+    if (p.kmode == K_LOWER) ke = min(ke, m0 + BM);
+    else if (p.kmode == K_UPPER) kb = m0;
+    if constexpr (EPI == EPI_PARTIAL) {
+      kb = blockIdx.y * p.k_chunk;
+      ke = min(ke, kb + p.k_chunk);
+    }
+    nk = ke > kb ? (ke - kb) / BK : 0;
+  }
+  auto issue = [&](int kt, uint4* la, uint4* lb) {
+    const bf16_t *a, *b;
+    if constexpr (KSEG > 1) {
+      const int seg = kt / nkd;
+      const int k0 = (kt - seg * nkd) * BK;
+      a = OA::advance(seg == 2 ? static_cast<const bf16_t*>(p.A2) + aoff : A, p.lda, k0);
+      b = OB::advance(seg == 1 ? static_cast<const bf16_t*>(p.B2) + boff : B, p.ldb, k0);
+    } else {
+      const int k0 = kb + kt * BK;
+      a = OA::advance(A, p.lda, k0);
+      b = OB::advance(B, p.ldb, k0);
+    }
+    oa.issue(a, la, wave);
+    ob.issue(b, lb, wave);
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // One K tile from LDS (As, Bs) while the next tile's loads (issue_next)
+  // are in flight. Each sub-step is a scheduling region: the next
+  // sub-step's fragment reads go first, then the MFMAs (sub-step 0 pairs
+  // the tile's global->LDS loads one per MFMA), so at most two sub-steps of
+  // fragments are live and every read has 16 MFMAs to land.
+  constexpr int NRD = (AK ? TM : 2 * TM) + (BKM ? TN : 2 * TN);  // LDS reads per sub-step
+  constexpr int NLD = OA::PER_WAVE + OB::PER_WAVE;                // global->LDS loads per tile
+  constexpr int MF = TM * TN;
+  auto compute = [&](const uint4* As, const uint4* Bs, auto&& issue_next) {
+    uint4 af[2][TM], bq[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = oa.frag(As, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bq[0][j] = ob.frag(Bs, wn * WTN + j * 32, 0, lane);
+    if constexpr (SCHED) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = oa.frag(As, wm * WTM + i * 32, ks + 1, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bq[cur ^ 1][j] = ob.frag(Bs, wn * WTN + j * 32, ks + 1, lane);
+      }
+      if (ks == 0) issue_next();
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) mma16(bq[cur][j], af[cur][i], acc[i][j], bf16_t{});
+      if constexpr (SCHED) {
+        if (ks + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+        if (ks == 0) {
+          sched_pairs<(NLD < MF ? NLD : MF), 0x020>();
+          if constexpr (MF > NLD) __builtin_amdgcn_sched_group_barrier(0x008, MF - NLD, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Past the last tile the prefetch repeats the last tile into the idle
+  // buffer (in bounds, never read), keeping the loop free of divergence.
+  if (nk > 0) issue(0, sa0, sb0);
+  wait_loads();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool odd = kt & 1;
+    const uint4* As = odd ? sa1 : sa0;
+    const uint4* Bs = odd ? sb1 : sb0;
+    uint4* An = odd ? sa0 : sa1;
+    uint4* Bn = odd ? sb0 : sb1;
+    compute(As, Bs, [&] { issue(min(kt + 1, nk - 1), An, Bn); });
+    wait_loads();
+    __syncthreads();
+  }
+
+  const int r32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm * WTM + i * 32 + r32;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = n0 + wn * WTN + j * 32 + jj * 8 + g * 4;
+        float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
+        if (row < p.M && col < p.N) epi_apply<EPI, bf16_t, TO>(p, z1, z2, row, col, v, blockIdx.y);
+      }
+    }
+  }
+}
+
+}  // namespace tpl

@@ -37,6 +37,7 @@
 #include "../../include/tp_layer.h"
 #include "aux_kernels.hpp"
 #include "gemm.hpp"
+#include "gemm_direct.hpp"
 
 using namespace tpl;
 
@@ -242,7 +243,17 @@ WsLayout ws_layout(const Dims& D, int blk) {
 
 enum Kind { KIND_BIG = 0, KIND_MID = 1 };
 
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE>
+// Does any K run of this GEMM end inside a K tile? (Then the kernel variant
+// that zero-fills k beyond the run is needed.) Runs start at 0, at m0 (a
+// multiple of BM, itself a multiple of BK), or at split-K chunk boundaries
+// (multiples of BK), and end at K, m0 + BM, a chunk boundary, or kseg_len.
+template <class Cfg>
+bool ragged_k(const GemmArgs& p, int kseg) {
+  if (kseg > 1) return p.kseg_len % Cfg::BK != 0;
+  return p.K % Cfg::BK != 0;
+}
+
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1>
 hipError_t launch(GemmArgs p, int batch, hipStream_t st) {
   p.tiles_m = cdiv(p.M, Cfg::BM);
   p.tiles_n = cdiv(p.N, Cfg::BN);
@@ -250,28 +261,54 @@ hipError_t launch(GemmArgs p, int batch, hipStream_t st) {
   if (p.zdiv <= 0) p.zdiv = 1;
   const int tiles = p.tri ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   if (tiles == 0 || batch == 0) return hipSuccess;
-  if constexpr (EPI != EPI_SOFTMAX_BWD) {
+  // bf16 tiles with whole 64-deep K steps take the direct global->LDS kernel
+  constexpr bool BF = sizeof(typename Cfg::T) == 2;
+  if constexpr (EPI != EPI_SOFTMAX_BWD && KSEG == 1) {
     if (p.splits > 1) {
       p.k_chunk = (int)(cdivl(cdivl(p.K, p.splits), Cfg::BK) * Cfg::BK);
-      hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI_PARTIAL, float, ROLE>), dim3(tiles, p.splits, 1),
-                         dim3(Cfg::NT), 0, st, p);
+      const dim3 grid(tiles, p.splits, 1);
+      bool done = false;
+      if constexpr (BF) {
+        if (!ragged_k<Cfg>(p, 1)) {
+          hipLaunchKernelGGL((gemm_direct_kernel<Cfg, AK, BKM, EPI_PARTIAL, float, ROLE, 1>), grid, dim3(Cfg::NT), 0,
+                             st, p);
+          done = true;
+        }
+      }
+      if (done) {
+      } else if (ragged_k<Cfg>(p, 1))
+        hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI_PARTIAL, float, ROLE, 1, true>), grid, dim3(Cfg::NT), 0,
+                           st, p);
+      else
+        hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI_PARTIAL, float, ROLE, 1, false>), grid, dim3(Cfg::NT), 0,
+                           st, p);
       const long n4 = (long)p.M * p.N / 4;
       hipLaunchKernelGGL((splitk_reduce_kernel<EPI, typename Cfg::T, TO, ROLE>), dim3((unsigned)cdivl(n4, 256)),
                          dim3(256), 0, st, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI, TO, ROLE>), dim3(tiles, 1, batch), dim3(Cfg::NT), 0, st, p);
+  const dim3 grid(tiles, 1, batch);
+  if constexpr (BF) {
+    if (!ragged_k<Cfg>(p, KSEG)) {
+      hipLaunchKernelGGL((gemm_direct_kernel<Cfg, AK, BKM, EPI, TO, ROLE, KSEG>), grid, dim3(Cfg::NT), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  if (ragged_k<Cfg>(p, KSEG))
+    hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI, TO, ROLE, KSEG, true>), grid, dim3(Cfg::NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<Cfg, AK, BKM, EPI, TO, ROLE, KSEG, false>), grid, dim3(Cfg::NT), 0, st, p);
   return hipGetLastError();
 }
 
 // One GEMM call site of the layer: fixed operand layout, epilogue and role;
 // the element type comes from the call's dtype.
-template <bool AK, bool BKM, int EPI, int ROLE, int KIND, bool OUTF32 = false>
+template <bool AK, bool BKM, int EPI, int ROLE, int KIND, bool OUTF32 = false, int KSEG = 1>
 hipError_t run(const Dims& D, GemmArgs p, int batch, hipStream_t st) {
   if (D.dt == TP_FP32) {
-    if constexpr (EPI == EPI_BIAS_SPLIT || EPI == EPI_DUAL_F32) {
-      return hipErrorInvalidValue;  // bf16-only epilogues
+    if constexpr (EPI == EPI_BIAS_SPLIT || EPI == EPI_DUAL_F32 || KSEG != 1) {
+      return hipErrorInvalidValue;  // bf16-only variants
     } else {
       p.splits = 1;
       return launch<CfgF32, AK, BKM, EPI, float, 0>(p, batch, st);
@@ -281,7 +318,7 @@ hipError_t run(const Dims& D, GemmArgs p, int batch, hipStream_t st) {
     return launch<CfgBig, AK, BKM, EPI, bf16_t, ROLE>(p, batch, st);
   } else {
     p.splits = 1;
-    return launch<CfgMid, AK, BKM, EPI, std::conditional_t<OUTF32, float, bf16_t>, ROLE>(p, batch, st);
+    return launch<CfgMid, AK, BKM, EPI, std::conditional_t<OUTF32, float, bf16_t>, ROLE, KSEG>(p, batch, st);
   }
 }
 
@@ -404,8 +441,10 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
       p.A2 = qkv_lo;
       p.B2 = B8(qkv_lo, (size_t)D.hr * D.es);
       p.kseg = 3; p.kseg_len = (int)D.d;
+      TRY((run<true, true, EPI_LINEAR, R_SCORES, KIND_MID, true, 3>(D, p, (int)D.z, st)));
+    } else {
+      TRY((run<true, true, EPI_LINEAR, R_SCORES, KIND_MID, true>(D, p, (int)D.z, st)));
     }
-    TRY((run<true, true, EPI_LINEAR, R_SCORES, KIND_MID, true>(D, p, (int)D.z, st)));
   }
   {  // P = causal softmax(S)
     prof::Scope sc(R_SOFTMAX, 0.0, (4.0 + es) * tri_elems(D), st);
