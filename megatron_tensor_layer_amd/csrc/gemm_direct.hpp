@@ -13,10 +13,10 @@
 //
 // LDS layouts (one 64-deep K tile):
 //  * K-contiguous operand: row = m (or n), 128 bytes = 64 k; the eight
-//    16-byte chunks of row r are stored at chunk ^ (r & 7). MFMA fragments
+//    16-byte chunks of row r are stored at chunk ^ kswz(r). MFMA fragments
 //    (8 consecutive k of one row) are single ds_read_b128, conflict free.
 //  * M/N-contiguous operand: row = k, BM*2 (BN*2) bytes of m (n); the 32-byte
-//    segments of row k are stored at segment ^ (k & 3). Fragments come from
+//    segments of row k are stored at segment ^ tsw(k). Fragments come from
 //    two ds_read_b64_tr_b16 per lane: within each 16-lane group, lane i gets
 //    element i%4 of the 8-byte chunks addressed by lanes 4c + i/4 (c = 0..3),
 //    so addressing rows k = 4c' + ... and columns 16*(g%2) + 4*(i%4) hands
@@ -65,6 +65,25 @@ __device__ __forceinline__ uint2 read_tr(const uint4* lds, uint32_t byte_off) {
 
 // One operand's tile loader + fragment reader. R = rows of the operand tile
 // along M (or N); KMAJ = operand stored K-contiguous in HBM.
+#ifndef TPL_KSWZ
+#define TPL_KSWZ 1
+#endif
+// XOR swizzle of the 16-byte chunks of K-contiguous LDS row `row`: distinct for
+// any 8 consecutive rows, and for the 8 even (odd) rows of any 16, so that a
+// ds_read_b128 of 32 consecutive rows is bank-conflict free whether the LDS
+// serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (TPL_KSWZ) return ((row >> 1) ^ ((row & 1) << 2)) & 7;
+  else return row & 7;
+}
+
+// Segment swizzle of M/N-contiguous rows: segment ^ tsw(k). The four k rows a
+// 16-lane group of ds_read_b64_tr_b16 touches land on four distinct segments
+// mod 4, and together with the neighbouring group's segment (s ^ 1) on eight
+// distinct segments, so the read is conflict free with 16 or 32 lanes per
+// LDS cycle.
+__device__ __forceinline__ int tsw(int k) { return (0x7520 >> (4 * (k & 3))) & 0xF; }
+
 template <bool KMAJ, int R, int NT>
 struct DirectOperand {
   static constexpr int BK = 64;
@@ -82,13 +101,13 @@ struct DirectOperand {
       const int inst = wave * PER_WAVE + i;
       if constexpr (KMAJ) {
         const int row = inst * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ (row & 7);
+        const int chunk = (lane & 7) ^ kswz(row);
         const int g = min(mn0 + row, lim - 1);
         off[i] = (uint32_t)((long)g * ld + chunk * 8);
       } else {
         constexpr int ROWS_PER_INST = 64 / ROW_UNITS;
         const int k = inst * ROWS_PER_INST + lane / ROW_UNITS;
-        const int unit = (lane % ROW_UNITS) ^ (2 * (k & 3));
+        const int unit = (lane % ROW_UNITS) ^ (2 * tsw(k));
         const int col = min(mn0 + unit * 8, lim - 8);
         off[i] = (uint32_t)((long)k * ld + col);
       }
@@ -107,7 +126,7 @@ struct DirectOperand {
   __device__ __forceinline__ uint4 frag(const uint4* lds, int r0, int ks, int lane) const {
     if constexpr (KMAJ) {
       const int row = r0 + (lane & 31);
-      return lds[row * 8 + ((2 * ks + (lane >> 5)) ^ (row & 7))];
+      return lds[row * 8 + ((2 * ks + (lane >> 5)) ^ kswz(row))];
     } else {
       const int g = lane >> 4, i = lane & 15;
       const int col = r0 + 16 * (g & 1) + 4 * (i & 3);
@@ -115,11 +134,11 @@ struct DirectOperand {
       uint2 lo, hi;
       {
         const int k = kb;
-        lo = read_tr(lds, (uint32_t)(k * R * 2 + (((col >> 3) ^ (2 * (k & 3))) << 4) + 2 * (col & 7)));
+        lo = read_tr(lds, (uint32_t)(k * R * 2 + (((col >> 3) ^ (2 * tsw(k))) << 4) + 2 * (col & 7)));
       }
       {
         const int k = kb + 4;
-        hi = read_tr(lds, (uint32_t)(k * R * 2 + (((col >> 3) ^ (2 * (k & 3))) << 4) + 2 * (col & 7)));
+        hi = read_tr(lds, (uint32_t)(k * R * 2 + (((col >> 3) ^ (2 * tsw(k))) << 4) + 2 * (col & 7)));
       }
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
@@ -130,7 +149,12 @@ struct DirectOperand {
 #define TPL_DIRECT_SCHED 0
 #endif
 
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED>
+#ifndef TPL_DIRECT_FENCE
+#define TPL_DIRECT_FENCE 1
+#endif
+
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED,
+          bool FENCE = TPL_DIRECT_FENCE>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_direct_kernel(const GemmArgs p) {
   static_assert(sizeof(typename Cfg::T) == 2, "direct path is bf16");
@@ -205,38 +229,31 @@ gemm_direct_kernel(const GemmArgs p) {
   constexpr int NRD = (AK ? TM : 2 * TM) + (BKM ? TN : 2 * TN);  // LDS reads per sub-step
   constexpr int NLD = OA::PER_WAVE + OB::PER_WAVE;                // global->LDS loads per tile
   constexpr int MF = TM * TN;
-  auto compute = [&](const uint4* As, const uint4* Bs, auto&& issue_next) {
-    uint4 af[2][TM], bq[2][TN];
+  // Software pipeline across the per-tile barrier: the MFMAs of a tile's last
+  // sub-step run after the barrier, while the first fragment reads of the
+  // next tile are in flight. Fragment registers alternate between two sets
+  // by sub-step; sub-step 3 and the next tile's sub-step 0 use different sets.
+  uint4 af[2][TM], bq[2][TN];
+  auto read_frags = [&](const uint4* As, const uint4* Bs, int ks, int set) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = oa.frag(As, wm * WTM + i * 32, 0, lane);
+    for (int i = 0; i < TM; ++i) af[set][i] = oa.frag(As, wm * WTM + i * 32, ks, lane);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bq[0][j] = ob.frag(Bs, wn * WTN + j * 32, 0, lane);
-    if constexpr (SCHED) __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < TN; ++j) bq[set][j] = ob.frag(Bs, wn * WTN + j * 32, ks, lane);
+  };
+  auto mfmas = [&](int set) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < 4) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = oa.frag(As, wm * WTM + i * 32, ks + 1, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bq[cur ^ 1][j] = ob.frag(Bs, wn * WTN + j * 32, ks + 1, lane);
-      }
-      if (ks == 0) issue_next();
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) mma16(bq[cur][j], af[cur][i], acc[i][j], bf16_t{});
-      if constexpr (SCHED) {
-        if (ks + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-        if (ks == 0) {
-          sched_pairs<(NLD < MF ? NLD : MF), 0x020>();
-          if constexpr (MF > NLD) __builtin_amdgcn_sched_group_barrier(0x008, MF - NLD, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int i = 0; i < TM; ++i) mma16(bq[set][j], af[set][i], acc[i][j], bf16_t{});
+  };
+  auto interleave = [&]() {
+    if constexpr (FENCE) {
+      sched_pairs<(NRD < MF ? NRD : MF), 0x100>();
+      if constexpr (MF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, MF - NRD, 0);
     }
+  };
+  auto fence = [&]() {
+    if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
   };
 
   // Past the last tile the prefetch repeats the last tile into the idle
@@ -244,16 +261,36 @@ gemm_direct_kernel(const GemmArgs p) {
   if (nk > 0) issue(0, sa0, sb0);
   wait_loads();
   __syncthreads();
+  if (nk > 0) read_frags(sa0, sb0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const bool odd = kt & 1;
     const uint4* As = odd ? sa1 : sa0;
     const uint4* Bs = odd ? sb1 : sb0;
     uint4* An = odd ? sa0 : sa1;
     uint4* Bn = odd ? sb0 : sb1;
-    compute(As, Bs, [&] { issue(min(kt + 1, nk - 1), An, Bn); });
+    fence();
+    read_frags(As, Bs, 1, 1);  // sub-step 0: MFMAs on set 0, reads of sub-step 1, next tile's loads
+    mfmas(0);
+    issue(min(kt + 1, nk - 1), An, Bn);
+    interleave();
+    fence();
+    read_frags(As, Bs, 2, 0);  // sub-step 1
+    mfmas(1);
+    interleave();
+    fence();
+    read_frags(As, Bs, 3, 1);  // sub-step 2
+    mfmas(0);
+    interleave();
+    fence();
     wait_loads();
     __syncthreads();
+    // sub-step 3 of this tile after the barrier, with sub-step 0 of the next
+    // tile's reads (the last iteration reads the idle buffer: in bounds, unused)
+    read_frags(An, Bn, 0, 0);
+    mfmas(1);
+    interleave();
   }
+  fence();
 
   const int r32 = lane & 31, g = lane >> 5;
 #pragma unroll
