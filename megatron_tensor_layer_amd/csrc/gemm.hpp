@@ -349,8 +349,7 @@ __device__ __forceinline__ void sched_substep() {
 // tile scheduling
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
-  int L = blockIdx.x;
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn, int L) {
   if (p.tri) {
     int m = (int)((sqrtf(8.0f * (float)L + 1.0f) - 1.0f) * 0.5f);
     while ((m + 1) * (m + 2) / 2 <= L) ++m;
@@ -389,7 +388,7 @@ __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1,
   const int wm = wave / Cfg::WN, wn = wave - (wave / Cfg::WN) * Cfg::WN;
 
   int tm, tn;
-  tile_coords(p, tm, tn);
+  tile_coords(p, tm, tn, blockIdx.x);
   const int m0 = tm * BM, n0 = tn * BN;
   const int z = blockIdx.z, z1 = z / p.zdiv, z2 = z - (z / p.zdiv) * p.zdiv;
   const long aoff = z1 * p.a_s1 + z2 * p.a_s2, boff = z1 * p.b_s1 + z2 * p.b_s2;

@@ -153,28 +153,25 @@ struct DirectOperand {
 #define TPL_DIRECT_FENCE 1
 #endif
 
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED,
-          bool FENCE = TPL_DIRECT_FENCE>
-__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_direct_kernel(const GemmArgs p) {
+// One output tile: linear tile index L (ordered by tile_coords), split-K
+// piece `split`, batch z. LDS buffers are passed in (two per operand).
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int KSEG, bool SCHED, bool FENCE>
+__device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split, int z, uint4* sa0, uint4* sb0,
+                                            uint4* sa1, uint4* sb1) {
   static_assert(sizeof(typename Cfg::T) == 2, "direct path is bf16");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BK = 64;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;
   using OA = DirectOperand<AK, BM, NT>;
   using OB = DirectOperand<BKM, BN, NT>;
-  __shared__ __attribute__((aligned(1024))) uint4 sa0[BM * 8];
-  __shared__ __attribute__((aligned(1024))) uint4 sb0[BN * 8];
-  __shared__ __attribute__((aligned(1024))) uint4 sa1[BM * 8];
-  __shared__ __attribute__((aligned(1024))) uint4 sb1[BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WN, wn = wave - (wave / Cfg::WN) * Cfg::WN;
 
   int tm, tn;
-  tile_coords(p, tm, tn);
+  tile_coords(p, tm, tn, L);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int z = blockIdx.z, z1 = z / p.zdiv, z2 = z - (z / p.zdiv) * p.zdiv;
+  const int z1 = z / p.zdiv, z2 = z - (z / p.zdiv) * p.zdiv;
   const long aoff = z1 * p.a_s1 + z2 * p.a_s2, boff = z1 * p.b_s1 + z2 * p.b_s2;
   const bf16_t* A = static_cast<const bf16_t*>(p.A) + aoff;
   const bf16_t* B = static_cast<const bf16_t*>(p.B) + boff;
@@ -192,7 +189,7 @@ gemm_direct_kernel(const GemmArgs p) {
     if (p.kmode == K_LOWER) ke = min(ke, m0 + BM);
     else if (p.kmode == K_UPPER) kb = m0;
     if constexpr (EPI == EPI_PARTIAL) {
-      kb = blockIdx.y * p.k_chunk;
+      kb = split * p.k_chunk;
       ke = min(ke, kb + p.k_chunk);
     }
     nk = ke > kb ? (ke - kb) / BK : 0;
@@ -227,7 +224,6 @@ gemm_direct_kernel(const GemmArgs p) {
   // the tile's global->LDS loads one per MFMA), so at most two sub-steps of
   // fragments are live and every read has 16 MFMAs to land.
   constexpr int NRD = (AK ? TM : 2 * TM) + (BKM ? TN : 2 * TN);  // LDS reads per sub-step
-  constexpr int NLD = OA::PER_WAVE + OB::PER_WAVE;                // global->LDS loads per tile
   constexpr int MF = TM * TN;
   // Software pipeline across the per-tile barrier: the MFMAs of a tile's last
   // sub-step run after the barrier, while the first fragment reads of the
@@ -302,9 +298,55 @@ gemm_direct_kernel(const GemmArgs p) {
       for (int jj = 0; jj < 4; ++jj) {
         const int col = n0 + wn * WTN + j * 32 + jj * 8 + g * 4;
         float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
-        if (row < p.M && col < p.N) epi_apply<EPI, bf16_t, TO>(p, z1, z2, row, col, v, blockIdx.y);
+        if (row < p.M && col < p.N) epi_apply<EPI, bf16_t, TO>(p, z1, z2, row, col, v, split);
       }
     }
+  }
+}
+
+#define TPL_DIRECT_LDS(BM, BN)                                 \
+  __shared__ __attribute__((aligned(1024))) uint4 sa0[BM * 8]; \
+  __shared__ __attribute__((aligned(1024))) uint4 sb0[BN * 8]; \
+  __shared__ __attribute__((aligned(1024))) uint4 sa1[BM * 8]; \
+  __shared__ __attribute__((aligned(1024))) uint4 sb1[BN * 8];
+
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED,
+          bool FENCE = TPL_DIRECT_FENCE>
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_direct_kernel(const GemmArgs p) {
+  TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
+  direct_tile<Cfg, AK, BKM, EPI, TO, KSEG, SCHED, FENCE>(p, blockIdx.x, blockIdx.y, blockIdx.z, sa0, sb0, sa1, sb1);
+}
+
+// Operand layouts and epilogue of one problem of a grouped launch.
+template <bool AK_, bool BK_, int EPI_, typename TO_>
+struct GemmKind {
+  static constexpr bool AK = AK_, BK = BK_;
+  static constexpr int EPI = EPI_;
+  using TO = TO_;
+};
+
+// Two independent GEMMs in one launch (a block's weight-gradient and input-
+// gradient products). Problem 0 has units0 = tiles0 x splits blocks (tile-
+// major over its split-K pieces), problem 1 tiles1 blocks; first1 selects
+// which problem's blocks come first. The host puts the longer K per tile
+// first, so the long tiles start first and the short ones fill in around
+// them (longest-processing-time order over the 256 CUs).
+template <class Cfg, class K0, class K1, int ROLE, bool SCHED = TPL_DIRECT_SCHED, bool FENCE = TPL_DIRECT_FENCE>
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_pair_kernel(const GemmArgs p0, const GemmArgs p1, int tiles0, int units0, int tiles1, int first1) {
+  TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
+  // blocks of the problem that goes first come first
+  int u = blockIdx.x;
+  const bool is0 = first1 ? (u >= tiles1) : (u < units0);
+  if (first1) u = is0 ? u - tiles1 : u + units0;
+  if (is0) {
+    const int split = u / tiles0;
+    direct_tile<Cfg, K0::AK, K0::BK, K0::EPI, typename K0::TO, 1, SCHED, FENCE>(p0, u - split * tiles0, split, 0, sa0,
+                                                                                 sb0, sa1, sb1);
+  } else {
+    direct_tile<Cfg, K1::AK, K1::BK, K1::EPI, typename K1::TO, 1, SCHED, FENCE>(p1, u - units0, 0, 0, sa0, sb0, sa1,
+                                                                                 sb1);
   }
 }
 

@@ -58,14 +58,16 @@ enum Role : int {
   R_QKV_FWD, R_SCORES, R_SOFTMAX, R_PV, R_O_FWD, R_FC1_FWD, R_FC2_FWD,
   R_FC2_DGRAD, R_FC2_WGRAD, R_DB2, R_FC1_DGRAD, R_FC1_WGRAD, R_DB1,
   R_O_DGRAD, R_O_WGRAD, R_DBO, R_ROWDOT, R_DS, R_DV, R_DQ, R_DK,
-  R_QKV_DGRAD, R_QKV_WGRAD, R_DBQKV, R_REDUCE, R_GEMM, R_COUNT
+  R_QKV_DGRAD, R_QKV_WGRAD, R_DBQKV, R_REDUCE, R_GEMM,
+  R_FC2_BWD, R_FC1_BWD, R_O_BWD, R_QKV_BWD, R_COUNT
 };
 
 const char* const kRoleName[R_COUNT] = {
   "qkv_fwd", "scores", "softmax", "pv", "o_fwd", "fc1_fwd", "fc2_fwd",
   "fc2_dgrad", "fc2_wgrad", "db2", "fc1_dgrad", "fc1_wgrad", "db1",
   "o_dgrad", "o_wgrad", "dbo", "rowdot", "ds", "dv", "dq", "dk",
-  "qkv_dgrad", "qkv_wgrad", "dbqkv", "reduce", "gemm"};
+  "qkv_dgrad", "qkv_wgrad", "dbqkv", "reduce", "gemm",
+  "fc2_dgrad+wgrad", "fc1_dgrad+wgrad", "o_dgrad+wgrad", "qkv_dgrad+wgrad"};
 
 namespace prof {
 struct Rec {
@@ -202,6 +204,34 @@ size_t partial_bytes(const Dims& D, long M, long N, long K) {
   return sp > 1 ? al((size_t)sp * M * N * 4) : 0;
 }
 
+// Grouped launch of two GEMMs (M0 x N0 x K0 first, M1 x N1 x K1 second):
+// problem 0 is split along K when its tiles run far longer than the average
+// work per CU, so that the split pieces and problem 1's tiles fill the
+// 256 CUs together. Returns the split count and its chunk (a multiple of BK).
+struct PairPlan {
+  int splits;
+  long chunk;
+};
+PairPlan pair_plan(long M0, long N0, long K0, long M1, long N1, long K1) {
+  const long t0 = cdivl(M0, CfgBig::BM) * cdivl(N0, CfgBig::BN);
+  const long t1 = cdivl(M1, CfgBig::BM) * cdivl(N1, CfgBig::BN);
+  const long it0 = cdivl(K0, CfgBig::BK), it1 = cdivl(K1, CfgBig::BK);
+  const double per_cu = ((double)t0 * it0 + (double)t1 * it1) / 256.0;
+  PairPlan P{1, K0};
+  if (it0 > 1.5 * per_cu && it0 >= 32) {
+    long sp = std::min<long>((long)std::ceil(it0 / per_cu), it0 / 16);
+    const long chunk = cdivl(it0, sp);
+    P.splits = (int)cdivl(it0, chunk);
+    P.chunk = chunk * CfgBig::BK;
+  }
+  return P;
+}
+size_t pair_partial_bytes(const Dims& D, long M0, long N0, long K0, long M1, long N1, long K1) {
+  if (D.dt != TP_BF16) return 0;
+  const PairPlan P = pair_plan(M0, N0, K0, M1, N1, K1);
+  return P.splits > 1 ? al((size_t)P.splits * M0 * N0 * 4) : 0;
+}
+
 struct WsLayout {
   size_t s, qkv_lo;         // attn fwd: fp32 scores, bf16 residuals of Q and K
   size_t dc, D, ds, dqkv;   // attn bwd
@@ -213,9 +243,15 @@ WsLayout ws_layout(const Dims& D, int blk) {
   WsLayout W{};
   size_t pb = 0;
   auto upd = [&](long M, long N, long K) { pb = std::max(pb, partial_bytes(D, M, N, K)); };
+  // input- and weight-gradient GEMMs of one weight, grouped
+  auto upd2 = [&](long M0, long N0, long K0, long M1, long N1, long K1) {
+    upd(M0, N0, K0);
+    upd(M1, N1, K1);
+    pb = std::max(pb, pair_partial_bytes(D, M0, N0, K0, M1, N1, K1));
+  };
   if (blk == TP_ATTN) {
     upd(D.T, D.q3, D.h); upd(D.T, D.h, D.hr);
-    upd(D.T, D.hr, D.h); upd(D.hr, D.h, D.T); upd(D.T, D.h, D.q3); upd(D.h, D.q3, D.T);
+    upd2(D.T, D.hr, D.h, D.hr, D.h, D.T); upd2(D.T, D.h, D.q3, D.h, D.q3, D.T);
     size_t fwd = al((size_t)D.z * D.s * D.s * 4);
     W.qkv_lo = fwd;
     if (D.dt == TP_BF16) fwd = al(fwd + (size_t)D.T * D.q3 * D.es);
@@ -228,7 +264,7 @@ WsLayout ws_layout(const Dims& D, int blk) {
     W.part = std::max(fwd, o);
   } else {
     upd(D.T, D.fr, D.h); upd(D.T, D.h, D.fr);
-    upd(D.T, D.fr, D.h); upd(D.fr, D.h, D.T); upd(D.T, D.h, D.fr); upd(D.h, D.fr, D.T);
+    upd2(D.T, D.fr, D.h, D.fr, D.h, D.T); upd2(D.T, D.h, D.fr, D.h, D.fr, D.T);
     W.du = 0;
     W.part = al((size_t)D.T * D.fr * D.es);
   }
@@ -330,6 +366,12 @@ GemmArgs gargs(long M, long N, long K) {
   return p;
 }
 
+#define TRY_E(x)                     \
+  do {                               \
+    hipError_t e_ = (x);             \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
 // Linear (weight) GEMM M x N x K: split-K chosen for the bf16 path.
 template <bool AK, bool BKM, int EPI, int ROLE>
 hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
@@ -341,6 +383,53 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
     p.part = part;
   }
   return run<AK, BKM, EPI, ROLE, KIND_BIG>(D, p, 1, st);
+}
+
+// A block's input-gradient GEMM (problem 0: dY W^T, K-contiguous operands,
+// epilogue E0) and weight-gradient GEMM (problem 1: X^T dY) in one launch
+// when both run on the direct bf16 kernel; otherwise two launches.
+template <int E0, int ROLE, int ROLE0, int ROLE1>
+hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_t st) {
+  using K0 = GemmKind<true, true, E0, bf16_t>;
+  using K1 = GemmKind<false, false, EPI_LINEAR, bf16_t>;
+  const bool direct = D.dt == TP_BF16 && !ragged_k<CfgBig>(p0, 1) && !ragged_k<CfgBig>(p1, 1);
+  if (!direct) {
+    TRY_E((linear<true, true, E0, ROLE0>(D, p0, part, st)));
+    return linear<false, false, EPI_LINEAR, ROLE1>(D, p1, part, st);
+  }
+  const double extra = (E0 == EPI_GELU_BWD) ? 1.0 : 0.0;
+  prof::Scope sc(ROLE, 2.0 * p0.M * p0.N * p0.K + 2.0 * p1.M * p1.N * p1.K,
+                 (double)D.es * ((double)p0.M * p0.K + (double)p0.K * p0.N + (1.0 + extra) * p0.M * p0.N +
+                                 (double)p1.M * p1.K + (double)p1.K * p1.N + (double)p1.M * p1.N),
+                 st);
+  for (GemmArgs* q : {&p0, &p1}) {
+    q->tiles_m = cdiv(q->M, CfgBig::BM);
+    q->tiles_n = cdiv(q->N, CfgBig::BN);
+    q->group_m = 8;
+    q->zdiv = 1;
+    q->splits = 1;
+  }
+  const int tiles0 = p0.tiles_m * p0.tiles_n, tiles1 = p1.tiles_m * p1.tiles_n;
+  const PairPlan P = pair_plan(p0.M, p0.N, p0.K, p1.M, p1.N, p1.K);
+  const int splits = P.splits;
+  if (splits > 1) {
+    p0.splits = splits;
+    p0.k_chunk = (int)P.chunk;
+    p0.part = part;
+  }
+  const int units0 = tiles0 * splits;
+  const int first1 = p1.K > P.chunk ? 1 : 0;
+  if (splits > 1) {
+    hipLaunchKernelGGL((gemm_pair_kernel<CfgBig, GemmKind<true, true, EPI_PARTIAL, float>, K1, ROLE>),
+                       dim3(units0 + tiles1), dim3(CfgBig::NT), 0, st, p0, p1, tiles0, units0, tiles1, first1);
+    const long n4 = (long)p0.M * p0.N / 4;
+    hipLaunchKernelGGL((splitk_reduce_kernel<E0, bf16_t, bf16_t, ROLE>), dim3((unsigned)cdivl(n4, 256)), dim3(256), 0,
+                       st, p0);
+  } else {
+    hipLaunchKernelGGL((gemm_pair_kernel<CfgBig, K0, K1, ROLE>), dim3(units0 + tiles1), dim3(CfgBig::NT), 0, st, p0,
+                       p1, tiles0, units0, tiles1, first1);
+  }
+  return hipGetLastError();
 }
 
 template <int ROLE>
@@ -497,14 +586,12 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     p.A = dy; p.lda = D.h;
     p.B = w->w_out; p.ldb = D.h;
     p.C = dC; p.ldc = D.hr;
-    TRY((linear<true, true, EPI_LINEAR, R_O_DGRAD>(D, p, part, st)));
-  }
-  {  // dWo_r = C^T dH
-    GemmArgs p = gargs(D.hr, D.h, D.T);
-    p.A = C; p.lda = D.hr;
-    p.B = dy; p.ldb = D.h;
-    p.C = g->dw_out; p.ldc = D.h;
-    TRY((linear<false, false, EPI_LINEAR, R_O_WGRAD>(D, p, part, st)));
+    // dWo_r = C^T dH
+    GemmArgs q = gargs(D.hr, D.h, D.T);
+    q.A = C; q.lda = D.hr;
+    q.B = dy; q.ldb = D.h;
+    q.C = g->dw_out; q.ldc = D.h;
+    TRY((pair<EPI_LINEAR, R_O_BWD, R_O_DGRAD, R_O_WGRAD>(D, p, q, part, st)));
   }
   TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, st));  // dbo (replica)
   {  // D = rowsum(dC * C) per (sequence, head, query)
@@ -560,14 +647,12 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     p.A = dqkv; p.lda = D.q3;
     p.B = w->w_in; p.ldb = D.q3;
     p.C = dx; p.ldc = D.h;
-    TRY((linear<true, true, EPI_LINEAR, R_QKV_DGRAD>(D, p, part, st)));
-  }
-  {  // dWqkv_r = X^T dQKV
-    GemmArgs p = gargs(D.h, D.q3, D.T);
-    p.A = x; p.lda = D.h;
-    p.B = dqkv; p.ldb = D.q3;
-    p.C = g->dw_in; p.ldc = D.q3;
-    TRY((linear<false, false, EPI_LINEAR, R_QKV_WGRAD>(D, p, part, st)));
+    // dWqkv_r = X^T dQKV
+    GemmArgs q = gargs(D.h, D.q3, D.T);
+    q.A = x; q.lda = D.h;
+    q.B = dqkv; q.ldb = D.q3;
+    q.C = g->dw_in; q.ldc = D.q3;
+    TRY((pair<EPI_LINEAR, R_QKV_BWD, R_QKV_DGRAD, R_QKV_WGRAD>(D, p, q, part, st)));
   }
   TRY(colsum<R_DBQKV>(D, dqkv, g->db_in, D.T, D.q3, D.q3, st));
   return TP_OK;
@@ -616,14 +701,12 @@ int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void*
     p.B = w->w_out; p.ldb = D.h;
     p.C = dU; p.ldc = D.fr;
     p.aux = U; p.ldx = D.fr;
-    TRY((linear<true, true, EPI_GELU_BWD, R_FC2_DGRAD>(D, p, part, st)));
-  }
-  {  // dW2_r = Z^T dY
-    GemmArgs p = gargs(D.fr, D.h, D.T);
-    p.A = Z; p.lda = D.fr;
-    p.B = dy; p.ldb = D.h;
-    p.C = g->dw_out; p.ldc = D.h;
-    TRY((linear<false, false, EPI_LINEAR, R_FC2_WGRAD>(D, p, part, st)));
+    // dW2_r = Z^T dY
+    GemmArgs q = gargs(D.fr, D.h, D.T);
+    q.A = Z; q.lda = D.fr;
+    q.B = dy; q.ldb = D.h;
+    q.C = g->dw_out; q.ldc = D.h;
+    TRY((pair<EPI_GELU_BWD, R_FC2_BWD, R_FC2_DGRAD, R_FC2_WGRAD>(D, p, q, part, st)));
   }
   TRY(colsum<R_DB2>(D, dy, g->db_out, D.T, D.h, D.h, st));  // db2 (replica)
   {  // dH_r = dU W1_r^T
@@ -631,14 +714,12 @@ int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void*
     p.A = dU; p.lda = D.fr;
     p.B = w->w_in; p.ldb = D.fr;
     p.C = dx; p.ldc = D.h;
-    TRY((linear<true, true, EPI_LINEAR, R_FC1_DGRAD>(D, p, part, st)));
-  }
-  {  // dW1_r = H^T dU
-    GemmArgs p = gargs(D.h, D.fr, D.T);
-    p.A = x; p.lda = D.h;
-    p.B = dU; p.ldb = D.fr;
-    p.C = g->dw_in; p.ldc = D.fr;
-    TRY((linear<false, false, EPI_LINEAR, R_FC1_WGRAD>(D, p, part, st)));
+    // dW1_r = H^T dU
+    GemmArgs q = gargs(D.h, D.fr, D.T);
+    q.A = x; q.lda = D.h;
+    q.B = dU; q.ldb = D.fr;
+    q.C = g->dw_in; q.ldc = D.fr;
+    TRY((pair<EPI_LINEAR, R_FC1_BWD, R_FC1_DGRAD, R_FC1_WGRAD>(D, p, q, part, st)));
   }
   TRY(colsum<R_DB1>(D, dU, g->db_in, D.T, D.fr, D.fr, st));
   return TP_OK;

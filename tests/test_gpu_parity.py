@@ -260,9 +260,13 @@ def test_profiler_attributes_every_role():
     full_layer_gpu(cfg)
     tp.tp_prof_enable(False)
     prof = tp.tp_prof_read()
-    roles = {"qkv_fwd", "scores", "softmax", "pv", "o_fwd", "fc1_fwd", "fc2_fwd", "fc2_dgrad", "fc2_wgrad", "db2",
-             "fc1_dgrad", "fc1_wgrad", "db1", "o_dgrad", "o_wgrad", "dbo", "rowdot", "ds", "dv", "dq", "dk",
-             "qkv_dgrad", "qkv_wgrad", "dbqkv", "reduce"}
+    roles = {"qkv_fwd", "scores", "softmax", "pv", "o_fwd", "fc1_fwd", "fc2_fwd", "db2", "db1", "dbo", "rowdot",
+             "ds", "dv", "dq", "dk", "dbqkv", "reduce"}
+    # a weight's input- and weight-gradient GEMMs run as one grouped launch
+    # when both take whole 64-deep K steps, else as two launches
+    for w in ("fc2", "fc1", "o", "qkv"):
+        grouped = f"{w}_dgrad+wgrad"
+        roles |= {grouped} if grouped in prof else {f"{w}_dgrad", f"{w}_wgrad"}
     assert roles <= set(prof)
     for name in roles - {"reduce"}:
         assert prof[name]["launches"] == cfg.t, name
