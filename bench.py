@@ -37,6 +37,58 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk x 2.4 GHz (AMD 
 PEAK_HBM_GBPS = 8000.0      # HBM3E, AMD MI355X spec
 DEFAULT_CONFIG = "gpt_175b"
 
+# A plain elementwise copy of known size (fp32 negation, COPY_BYTES read and
+# COPY_BYTES written), launched once before the warm-up so that a counter
+# run of this script sees the copy beside the layer's kernels and can scale
+# FETCH_SIZE / WRITE_SIZE to bytes.
+COPY_BYTES = 1 << 30
+
+# Sources of the GEMM kernels and their launch plan: a traffic figure taken
+# from counters is reported only while these files are unchanged.
+KERNEL_SOURCES = ("megatron_tensor_layer_amd/csrc/gemm.hpp", "megatron_tensor_layer_amd/csrc/gemm_direct.hpp",
+                  "megatron_tensor_layer_amd/csrc/tp_common.hpp", "megatron_tensor_layer_amd/csrc/tp_layer.hip")
+
+
+def kernel_sources_digest():
+    import hashlib
+    hs = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            hs.update(f.read())
+    return hs.hexdigest()
+
+
+def measured_traffic(config, role):
+    """HBM bytes per launch of `role` from the committed counter summary
+    profiles/<config>_<role>_traffic.txt ('+' in the role written '_'), or
+    None when there is no summary for this role or the kernel sources changed
+    since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{config}_{role.replace('+', '_')}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("role") != role or kv.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
 
 def model_flops_per_rank(h, s, b, t):
     return 72.0 * b * s * h * h * (1.0 + s / (6.0 * h)) / t
@@ -173,6 +225,7 @@ def main():
     cfg = I.CONFIGS[args.config]
     h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
     layer, X, dY = build_layer(cfg)
+    copy_calibration()
     for _ in range(args.warmup):
         layer.forward(X)
         layer.backward(dY)
@@ -204,9 +257,12 @@ def main():
     de = prof[dom]
     per_launch_ms = de["ms"] / de["launches"]
     achieved = de["flops"] / de["launches"] / (per_launch_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": f"gemm_kernel role {dom}", "achieved": round(achieved, 1),
+    traffic = measured_traffic(cfg.name, dom)
+    roofline = {"bound": "mfma", "kernel": f"GEMM role {dom}", "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "flops_per_launch": de["flops"] / de["launches"],
+                "traffic": traffic, "traffic_unit": "bytes per launch (HBM, counters)",
+                "algorithmic_bytes_per_launch": de["bytes"] / de["launches"],
+                "flops_per_launch": de["flops"] / de["launches"],
                 "ms_per_launch": round(per_launch_ms, 4)}
 
     out = {
