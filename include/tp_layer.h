@@ -137,17 +137,24 @@ int tp_layer_bwd(int h, int a, int s, int b, int t, int rank, int dtype, int blo
 int tp_reduce_partials(int dtype, long rows, long cols, int t, const void *partials, const void *bias,
                        const void *residual, void *out, void *stream);
 
-/* General GEMM on the same MFMA kernels: C[M,N] = alpha * op(A) op(B) (+ bias[N]).
+/* General GEMM on the same MFMA kernels and the same launch planning as the
+ * layer's weight GEMMs (whole waves of 256x256 tiles, stream-K over a partial
+ * last wave, or split-K for few tiles; every sum in a fixed order):
+ *   C[M,N] = alpha * op(A) op(B) (+ bias[N]).
  *   a_kmajor: A stored [M, lda] (element (m,k) at A[m*lda+k]) if 1, else
  *             stored [K, lda] (element (m,k) at A[k*lda+m]).
  *   b_kmajor: B stored [N, ldb] (element (k,n) at B[n*ldb+k]) if 1, else
  *             stored [K, ldb] (element (k,n) at B[k*ldb+n]).
  *   bias may be NULL. C has leading dimension ldc. M, N, K multiples of 16;
- *   leading dimensions multiples of 8. Used by the tests to check each
- *   operand layout on its own.                                               */
+ *   leading dimensions multiples of 8.
+ *   workspace: device scratch of at least tp_gemm_workspace_bytes(dtype, M,
+ *   N, K) bytes, 256-byte aligned, owned by the caller (NULL when that size is
+ *   0); TP_EWORKSPACE if smaller. Used by the tests to check each operand
+ *   layout and launch plan on its own.                                        */
+size_t tp_gemm_workspace_bytes(int dtype, int M, int N, int K);
 int tp_gemm(int dtype, int M, int N, int K, float alpha,
             const void *A, long lda, int a_kmajor, const void *B, long ldb, int b_kmajor,
-            const void *bias, void *C, long ldc, void *stream);
+            const void *bias, void *C, long ldc, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Opt-in profiling of the library's own launches. While enabled, every
  * kernel group the library enqueues (one GEMM with its split-K reduction,

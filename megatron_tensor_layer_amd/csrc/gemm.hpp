@@ -44,7 +44,8 @@ enum EpiKind : int {
   EPI_PARTIAL = 4,      // split-K: fp32 partial[split, m, n] = acc
   EPI_BIAS_SPLIT = 5,   // V = acc + bias[n] -> C (bf16); for n < c2_cols also the
                         // rounding residual V - bf16(V) -> C2 (bf16), same layout
-  EPI_DUAL_F32 = 6      // C = acc (storage type) and C2 = acc (fp32), same layout
+  EPI_DUAL_F32 = 6,     // C = acc (storage type) and C2 = acc (fp32), same layout
+  EPI_SK_PART = 7       // fp32 accumulator fragment of a stream-K unit, in register order
 };
 
 enum KMode : int {
@@ -61,6 +62,7 @@ struct GemmArgs {
   int kmode;
   int splits, k_chunk;   // split-K (EPI_PARTIAL pass)
   int group_m;           // tile-rows per ordering group
+  int no_xcd;            // 1: tile index is used as given (the launch maps blocks to XCDs itself)
   int kseg, kseg_len;    // kseg = 3: K runs over (A,B), (A,B2), (A2,B), each kseg_len long
   int c2_cols;           // EPI_BIAS_SPLIT: columns that get a residual in C2
   const void* A; long lda, a_s1, a_s2;
@@ -74,6 +76,18 @@ struct GemmArgs {
   const void* aux; long ldx, x_s1, x_s2;
   const float* rowv; long r_s1, r_s2;
   float alpha;
+  float* part;
+};
+
+// Stream-K launch plan (direct bf16 kernel, batch 1). Blocks [0, dp_tiles)
+// compute whole tiles; the remaining sk_tiles tiles' K iterations (iters of
+// BK each per tile) are laid end to end and cut into `units` runs of c
+// iterations, one run per block. A run that covers only part of a tile
+// stores its fp32 fragment in slot (unit - first unit of the tile) of that
+// tile's f slots; the fix-up kernel sums the slots in order and applies the
+// epilogue. dp_tiles and units are multiples of 8 (one run of blocks per XCD).
+struct SkPlan {
+  int dp_tiles, sk_tiles, iters, c, units, f;
   float* part;
 };
 
@@ -359,7 +373,7 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn,
     return;
   }
   const int tiles = p.tiles_m * p.tiles_n;
-  if ((tiles & 7) == 0) L = (L & 7) * (tiles >> 3) + (L >> 3);  // same-XCD runs of tiles
+  if ((tiles & 7) == 0 && !p.no_xcd) L = (L & 7) * (tiles >> 3) + (L >> 3);  // same-XCD runs of tiles
   const int per_group = p.group_m * p.tiles_n;
   const int grp = L / per_group, first = grp * p.group_m;
   const int gs = min(p.tiles_m - first, p.group_m);

@@ -155,9 +155,12 @@ struct DirectOperand {
 
 // One output tile: linear tile index L (ordered by tile_coords), split-K
 // piece `split`, batch z. LDS buffers are passed in (two per operand).
+// EPI_SK_PART: K range [kb_, ke_) and the fragment goes to skdst in register
+// order (float4 index ((wave TM + i) TN + j) 4 + jj) 64 + lane).
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int KSEG, bool SCHED, bool FENCE>
 __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split, int z, uint4* sa0, uint4* sb0,
-                                            uint4* sa1, uint4* sb1) {
+                                            uint4* sa1, uint4* sb1, int kb_ = 0, int ke_ = 0,
+                                            float* skdst = nullptr) {
   static_assert(sizeof(typename Cfg::T) == 2, "direct path is bf16");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BK = 64;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;
@@ -191,6 +194,9 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     if constexpr (EPI == EPI_PARTIAL) {
       kb = split * p.k_chunk;
       ke = min(ke, kb + p.k_chunk);
+    } else if constexpr (EPI == EPI_SK_PART) {
+      kb = kb_;
+      ke = ke_;
     }
     nk = ke > kb ? (ke - kb) / BK : 0;
   }
@@ -288,6 +294,18 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   }
   fence();
 
+  if constexpr (EPI == EPI_SK_PART) {
+    float4* dst = reinterpret_cast<float4*>(skdst) + wave * (TM * TN * 256) + lane;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          dst[((i * TN + j) * 4 + jj) * 64] =
+              make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
+    return;
+  }
   const int r32 = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -316,6 +334,68 @@ __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1,
 gemm_direct_kernel(const GemmArgs p) {
   TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
   direct_tile<Cfg, AK, BKM, EPI, TO, KSEG, SCHED, FENCE>(p, blockIdx.x, blockIdx.y, blockIdx.z, sa0, sb0, sa1, sb1);
+}
+
+// Stream-K launch (plan in SkPlan). Consecutive blocks go to different XCDs,
+// so block b is remapped to (b mod 8) * (n / 8) + b / 8: each XCD takes one
+// contiguous run of whole tiles and one contiguous run of stream-K units,
+// and the tiles of a run share operand panels in that XCD's L2.
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, bool SCHED = TPL_DIRECT_SCHED,
+          bool FENCE = TPL_DIRECT_FENCE>
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_sk_kernel(const GemmArgs p, const SkPlan s) {
+  TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
+  const int b = blockIdx.x;
+  if (b < s.dp_tiles) {
+    const int L = (b & 7) * (s.dp_tiles >> 3) + (b >> 3);
+    direct_tile<Cfg, AK, BKM, EPI, TO, 1, SCHED, FENCE>(p, L, 0, 0, sa0, sb0, sa1, sb1);
+    return;
+  }
+  const int sb = b - s.dp_tiles;
+  const int u = (sb & 7) * (s.units >> 3) + (sb >> 3);
+  const long total = (long)s.sk_tiles * s.iters;
+  long it = (long)u * s.c;
+  const long end = min(it + s.c, total);
+  while (it < end) {
+    const int j = (int)(it / s.iters);
+    const int k0 = (int)(it - (long)j * s.iters);
+    const int k1 = (int)min((long)s.iters, k0 + (end - it));
+    const int slot = u - (int)(((long)j * s.iters) / s.c);
+    float* dst = s.part + ((long)j * s.f + slot) * (long)(Cfg::BM * Cfg::BN);
+    direct_tile<Cfg, AK, BKM, EPI_SK_PART, float, 1, SCHED, FENCE>(p, s.dp_tiles + j, 0, 0, sa0, sb0, sa1, sb1,
+                                                                   k0 * 64, k1 * 64, dst);
+    it += k1 - k0;
+    __syncthreads();  // the next run's first loads reuse this run's LDS buffers
+  }
+}
+
+// Stream-K fix-up: for each tile of the stream-K region, the fixed-order sum
+// of its fragments, then the epilogue. One float4 of the tile per thread, in
+// the fragments' register order.
+template <class Cfg, int EPI, typename TO, int ROLE>
+__global__ void __launch_bounds__(256) sk_fixup_kernel(const GemmArgs p, const SkPlan s) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, TM = Cfg::TM, TN = Cfg::TN;
+  const int j = blockIdx.y;
+  const int q = blockIdx.x * 256 + threadIdx.x;  // float4 index within the tile
+  const int lane = q & 63, jj = (q >> 6) & 3;
+  int r = q >> 8;
+  const int jn = r % TN;
+  r /= TN;
+  const int i = r % TM, wave = r / TM;
+  const int wm = wave / Cfg::WN, wn = wave - (wave / Cfg::WN) * Cfg::WN;
+  int tm, tn;
+  tile_coords(p, tm, tn, s.dp_tiles + j);
+  const int row = tm * BM + wm * Cfg::WTM + i * 32 + (lane & 31);
+  const int col = tn * BN + wn * Cfg::WTN + jn * 32 + jj * 8 + (lane >> 5) * 4;
+  if (row >= p.M || col >= p.N) return;
+  const int uf = (int)(((long)j * s.iters) / s.c), ul = (int)(((long)(j + 1) * s.iters - 1) / s.c);
+  const float4* src = reinterpret_cast<const float4*>(s.part + (long)j * s.f * (BM * BN)) + q;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k <= ul - uf; ++k) {
+    const float4 x = src[(long)k * (BM * BN / 4)];
+    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+  }
+  epi_apply<EPI, bf16_t, TO>(p, 0, 0, row, col, v, 0);
 }
 
 // Operand layouts and epilogue of one problem of a grouped launch.

@@ -198,10 +198,47 @@ SavedLayout saved_layout(const Dims& D, int blk) {
   return L;
 }
 
+// Stream-K plan for a bf16 GEMM on 256x256 tiles with whole 64-deep K steps
+// (units = 0: not worth it). Whole waves of tiles run as they are; the last,
+// partial wave's K iterations are spread over all 256 CUs. Chosen when the
+// modelled time beats the plain (or split-K) launch; the model counts one
+// tile-iteration as ~1.95 us and charges the fp32 fragments' write + read at
+// ~5 TB/s plus a launch gap for the fix-up.
+SkPlan sk_plan(long M, long N, long K) {
+  SkPlan s{};
+  if (K % CfgBig::BK != 0) return s;
+  const long tiles = cdivl(M, CfgBig::BM) * cdivl(N, CfgBig::BN);
+  const long I = K / CfgBig::BK;
+  const long W = tiles / 256, R = tiles % 256;
+  if (R == 0 || I < 8) return s;
+  const double t_it = 1.95e-6, frag = 4.0 * CfgBig::BM * CfgBig::BN;
+  double plain = (double)cdivl(tiles, 256) * I * t_it;
+  const int sp = choose_splits(M, N, K);
+  if (sp > 1) {
+    const long chunk = cdivl(I, sp);
+    plain = (double)cdivl(tiles * sp, 256) * chunk * t_it + 2.0 * sp * M * N * 4.0 / 5e12 + 5e-6;
+  }
+  const long c = cdivl(R * I, 256);
+  const double sk = (double)(W * I + c) * t_it + 2.0 * (256 + R) * frag / 5e12 + 5e-6;
+  if (sk >= 0.97 * plain) return s;
+  s.dp_tiles = (int)(W * 256);
+  s.sk_tiles = (int)R;
+  s.iters = (int)I;
+  s.c = (int)c;
+  s.units = 256;
+  int f = 1;
+  for (long j = 0; j < R; ++j) f = std::max<int>(f, (int)(((j + 1) * I - 1) / c - (j * I) / c + 1));
+  s.f = f;
+  return s;
+}
+
 size_t partial_bytes(const Dims& D, long M, long N, long K) {
   if (D.dt != TP_BF16) return 0;
   const int sp = choose_splits(M, N, K);
-  return sp > 1 ? al((size_t)sp * M * N * 4) : 0;
+  size_t b = sp > 1 ? al((size_t)sp * M * N * 4) : 0;
+  const SkPlan s = sk_plan(M, N, K);
+  if (s.units) b = std::max(b, al((size_t)s.sk_tiles * s.f * CfgBig::BM * CfgBig::BN * 4));
+  return b;
 }
 
 // Grouped launch of two GEMMs (M0 x N0 x K0 first, M1 x N1 x K1 second):
@@ -379,6 +416,20 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
   prof::Scope sc(ROLE, 2.0 * p.M * p.N * p.K,
                  (double)D.es * ((double)p.M * p.K + (double)p.K * p.N + (1.0 + extra) * p.M * p.N), st);
   if (D.dt == TP_BF16) {
+    SkPlan s = sk_plan(p.M, p.N, p.K);
+    if (s.units) {
+      s.part = part;
+      p.tiles_m = cdiv(p.M, CfgBig::BM);
+      p.tiles_n = cdiv(p.N, CfgBig::BN);
+      p.group_m = 8;
+      p.no_xcd = 1;
+      p.splits = 1;
+      hipLaunchKernelGGL((gemm_sk_kernel<CfgBig, AK, BKM, EPI, bf16_t, ROLE>), dim3(s.dp_tiles + s.units),
+                         dim3(CfgBig::NT), 0, st, p, s);
+      hipLaunchKernelGGL((sk_fixup_kernel<CfgBig, EPI, bf16_t, ROLE>),
+                         dim3(CfgBig::BM * CfgBig::BN / 4 / 256, s.sk_tiles), dim3(256), 0, st, p, s);
+      return hipGetLastError();
+    }
     p.splits = choose_splits(p.M, p.N, p.K);
     p.part = part;
   }
@@ -804,8 +855,14 @@ int tp_reduce_partials(int dtype, long rows, long cols, int t, const void* parti
   return e == hipSuccess ? TP_OK : hip_fail(e);
 }
 
+size_t tp_gemm_workspace_bytes(int dtype, int M, int N, int K) {
+  if ((dtype != TP_BF16 && dtype != TP_FP32) || M <= 0 || N <= 0 || K <= 0) return 0;
+  return partial_bytes(make_dims(16, 1, 16, 1, 1, dtype), M, N, K);
+}
+
 int tp_gemm(int dtype, int M, int N, int K, float alpha, const void* A, long lda, int a_kmajor, const void* B, long ldb,
-            int b_kmajor, const void* bias, void* C, long ldc, void* stream) {
+            int b_kmajor, const void* bias, void* C, long ldc, void* workspace, size_t workspace_bytes,
+            void* stream) {
   if (dtype != TP_BF16 && dtype != TP_FP32) return TP_EINVAL;
   if (M <= 0 || N <= 0 || K <= 0) return TP_EINVAL;
   if (M % 16 || N % 16 || K % 16 || lda % 8 || ldb % 8 || ldc % 8) return TP_EUNSUPPORTED;
@@ -813,16 +870,20 @@ int tp_gemm(int dtype, int M, int N, int K, float alpha, const void* A, long lda
   if (!A || !B || !C) return TP_ENULL;
   if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias)) return TP_EALIGN;
   const Dims D = make_dims(16, 1, 16, 1, 1, dtype);  // only the dtype is used
+  const size_t need = partial_bytes(D, M, N, K);
+  if (workspace_bytes < need) return TP_EWORKSPACE;
+  if (need && !workspace) return TP_ENULL;
+  if (misaligned(workspace)) return TP_EALIGN;
   GemmArgs p = gargs(M, N, K);
   p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C; p.ldc = ldc;
   p.bias = bias; p.alpha = alpha;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  prof::Scope sc(R_GEMM, 2.0 * M * N * K, (double)D.es * ((double)M * K + (double)K * N + (double)M * N), st);
+  float* part = static_cast<float*>(workspace);
   hipError_t e;
-  if (a_kmajor && !b_kmajor) e = run<true, false, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
-  else if (a_kmajor && b_kmajor) e = run<true, true, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
-  else if (!a_kmajor && !b_kmajor) e = run<false, false, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
-  else e = run<false, true, EPI_LINEAR, R_GEMM, KIND_BIG>(D, p, 1, st);
+  if (a_kmajor && !b_kmajor) e = linear<true, false, EPI_LINEAR, R_GEMM>(D, p, part, st);
+  else if (a_kmajor && b_kmajor) e = linear<true, true, EPI_LINEAR, R_GEMM>(D, p, part, st);
+  else if (!a_kmajor && !b_kmajor) e = linear<false, false, EPI_LINEAR, R_GEMM>(D, p, part, st);
+  else e = linear<false, true, EPI_LINEAR, R_GEMM>(D, p, part, st);
   return e == hipSuccess ? TP_OK : hip_fail(e);
 }
 

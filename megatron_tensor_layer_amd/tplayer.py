@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtplayer.
 
 # every symbol include/tp_layer.h declares
 EXPORTS = ("tp_check_args", "tp_saved_bytes", "tp_workspace_bytes", "tp_layer_fwd", "tp_layer_bwd",
-           "tp_reduce_partials", "tp_gemm", "tp_prof_enable", "tp_prof_read", "tp_strerror")
+           "tp_reduce_partials", "tp_gemm_workspace_bytes", "tp_gemm", "tp_prof_enable", "tp_prof_read", "tp_strerror")
 
 _lib = None
 
@@ -72,7 +72,9 @@ def lib():
     L.tp_reduce_partials.restype = i
     L.tp_prof_enable.argtypes, L.tp_prof_enable.restype = [i], i
     L.tp_prof_read.argtypes, L.tp_prof_read.restype = [ctypes.POINTER(TPProfEntry), i], i
-    L.tp_gemm.argtypes = [i, i, i, i, f32, vp, lng, i, vp, lng, i, vp, vp, lng, vp]
+    L.tp_gemm_workspace_bytes.argtypes = [i, i, i, i]
+    L.tp_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.tp_gemm.argtypes = [i, i, i, i, f32, vp, lng, i, vp, lng, i, vp, vp, lng, vp, ctypes.c_size_t, vp]
     L.tp_gemm.restype = i
     L.tp_strerror.argtypes, L.tp_strerror.restype = [i], ctypes.c_char_p
     _lib = L
@@ -196,6 +198,16 @@ def tp_prof_read():
                                    "bytes": buf[i].bytes} for i in range(min(n, 64))}
 
 
-def tp_gemm(dtype, M, N, K, alpha, A, lda, a_kmajor, B, ldb, b_kmajor, bias, C, ldc, stream=None):
+def tp_gemm_workspace_bytes(dtype, M, N, K):
+    return int(lib().tp_gemm_workspace_bytes(dtype, M, N, K))
+
+
+def tp_gemm(dtype, M, N, K, alpha, A, lda, a_kmajor, B, ldb, b_kmajor, bias, C, ldc, workspace=None, stream=None):
+    """C = alpha op(A) op(B) (+ bias). `workspace`: a device tensor of at least
+    tp_gemm_workspace_bytes(dtype, M, N, K) bytes, allocated here if None."""
+    need = tp_gemm_workspace_bytes(dtype, M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=C.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().tp_gemm(dtype, M, N, K, alpha, _ptr(A), lda, int(a_kmajor), _ptr(B), ldb, int(b_kmajor),
-                         _ptr(bias), _ptr(C), ldc, _stream(stream)), "tp_gemm")
+                         _ptr(bias), _ptr(C), ldc, _ptr(workspace), nbytes, _stream(stream)), "tp_gemm")

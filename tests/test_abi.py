@@ -109,8 +109,18 @@ def test_reduce_and_gemm_validation_on_host():
     assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, none, none, none, a, None) == tp.TP_ENULL
     assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, _fake(0x100002), none, none, a, None) == tp.TP_EALIGN
     assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, a, _fake(0x100008), none, a, None) == tp.TP_EALIGN
-    assert L.tp_gemm(tp.TP_BF16, 20, 16, 16, 1.0, a, 16, 1, a, 16, 1, None, a, 16, None) == tp.TP_EUNSUPPORTED
-    assert L.tp_gemm(tp.TP_BF16, 16, 16, 32, 1.0, a, 16, 1, a, 32, 1, None, a, 16, None) == tp.TP_EINVAL  # lda < K
+    assert L.tp_gemm(tp.TP_BF16, 20, 16, 16, 1.0, a, 16, 1, a, 16, 1, None, a, 16, None, 0, None) == tp.TP_EUNSUPPORTED
+    assert L.tp_gemm(tp.TP_BF16, 16, 16, 32, 1.0, a, 16, 1, a, 32, 1, None, a, 16, None, 0, None) == tp.TP_EINVAL
+    # stream-K over a partial last wave needs fp32 fragment slots: workspace checked before any launch
+    M, N, K = 2048, 6144, 12288
+    need = tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K)
+    assert need >= 192 * 2 * 256 * 256 * 4
+    assert L.tp_gemm(tp.TP_BF16, M, N, K, 1.0, a, K, 1, a, N, 0, None, a, N, a, need - 256, None) == tp.TP_EWORKSPACE
+    assert L.tp_gemm(tp.TP_BF16, M, N, K, 1.0, a, K, 1, a, N, 0, None, a, N, none, need, None) == tp.TP_ENULL
+    # small problems need none; fp32 never does
+    assert tp.tp_gemm_workspace_bytes(tp.TP_BF16, 256, 256, 256) == 0
+    assert tp.tp_gemm_workspace_bytes(tp.TP_FP32, M, N, K) == 0
+    assert tp.tp_gemm_workspace_bytes(tp.TP_BF16, 0, N, K) == 0
 
 
 def test_profiler_without_gpu_work():

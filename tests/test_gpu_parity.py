@@ -52,6 +52,42 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
     assert rel_err(to_np(C), ref) <= tol
 
 
+# Launch plans at full size: stream-K over a partial last wave (with and
+# without whole waves before it, ragged M and N, 3 and 6 fragments per tile)
+# and split-K. Rows sampled (first, last, scattered), every column, fp64
+# reference from the same bf16 operands; a second call must match bitwise.
+@pytest.mark.parametrize("M,N,K,ak,bk", [
+    (2064, 4624, 12288, 1, 0),   # 171 tiles < one wave: all stream-K (c = 129 of 192 iterations)
+    (2064, 4624, 12288, 1, 1),
+    (2064, 8208, 6144, 0, 0),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
+    (2064, 8208, 6144, 0, 1),
+    (1040, 2832, 4096, 1, 0),    # 60 tiles: split-K
+])
+def test_gemm_launch_plans_full_size(M, N, K, ak, bk):
+    print(f"gemm plan {M}x{N}x{K} ak={ak} bk={bk}", flush=True)
+    rng = np.random.default_rng(M + N + K + 2 * ak + bk)
+    A = I.round_to_bf16(rng.standard_normal((M, K), dtype=np.float32))
+    B = I.round_to_bf16(rng.standard_normal((K, N), dtype=np.float32))
+    bias = I.round_to_bf16(rng.standard_normal(N, dtype=np.float32))
+    bf = torch.bfloat16
+    Ad = torch.from_numpy(A if ak else np.ascontiguousarray(A.T)).to("cuda", bf)
+    Bd = torch.from_numpy(np.ascontiguousarray(B.T) if bk else B).to("cuda", bf)
+    bd = torch.from_numpy(bias).to("cuda", bf)
+    assert tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K) > 0
+    outs = []
+    for _ in range(2):
+        C = torch.full((M, N), float("nan"), device="cuda", dtype=bf)
+        tp.tp_gemm(tp.TP_BF16, M, N, K, 0.5, Ad, K if ak else M, ak, Bd, K if bk else N, bk, bd, C, N)
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 16, M - 1], rng.integers(0, M, 59)]))
+    ref = 0.5 * (A[rows].astype(np.float64) @ B.astype(np.float64)) + bias
+    got = outs[0][torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= 8e-3
+
+
 # ---------------------------------------------------------------------------
 # whole layer, all ranks, element by element
 # ---------------------------------------------------------------------------
