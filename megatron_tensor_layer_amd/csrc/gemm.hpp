@@ -392,7 +392,7 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn,
 // KSEG = 3 runs the K loop over (A, B), (A, B2) and (A2, B) in turn.
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool TAIL = false,
           bool SCHED = true>
-__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) gemm_kernel(const GemmArgs p) {
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256))) gemm_kernel(const GemmArgs p) {
   using T = typename Cfg::T;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BK = Cfg::BK;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;

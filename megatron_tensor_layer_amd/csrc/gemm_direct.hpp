@@ -118,6 +118,9 @@ struct DirectOperand {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) load_lds16(base, off[i] * 2u, lds + (wave * PER_WAVE + i) * 64);
   }
+  __device__ __forceinline__ void issue_one(const bf16_t* base, uint4* lds, int wave, int i) const {
+    load_lds16(base, off[i] * 2u, lds + (wave * PER_WAVE + i) * 64);
+  }
   __device__ __forceinline__ static const bf16_t* advance(const bf16_t* base, long ld, int k) {
     return KMAJ ? base + k : base + (long)k * ld;
   }
@@ -151,6 +154,21 @@ struct DirectOperand {
 
 #ifndef TPL_DIRECT_FENCE
 #define TPL_DIRECT_FENCE 1
+#endif
+#ifndef TPL_DMA_SPREAD
+#define TPL_DMA_SPREAD 0
+#endif
+#ifndef TPL_SLOTS
+#define TPL_SLOTS 1
+#endif
+#ifndef TPL_SLOT_DMA_SUBS
+#define TPL_SLOT_DMA_SUBS 2
+#endif
+#ifndef TPL_SLOT_EARLY
+#define TPL_SLOT_EARLY 1
+#endif
+#ifndef TPL_DMA_EVERY
+#define TPL_DMA_EVERY 2
 #endif
 
 // One output tile: linear tile index L (ordered by tile_coords), split-K
@@ -200,6 +218,18 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     }
     nk = ke > kb ? (ke - kb) / BK : 0;
   }
+  auto next_ptrs = [&](int kt, const bf16_t*& a, const bf16_t*& b) {
+    if constexpr (KSEG > 1) {
+      const int seg = kt / nkd;
+      const int k0 = (kt - seg * nkd) * BK;
+      a = OA::advance(seg == 2 ? static_cast<const bf16_t*>(p.A2) + aoff : A, p.lda, k0);
+      b = OB::advance(seg == 1 ? static_cast<const bf16_t*>(p.B2) + boff : B, p.ldb, k0);
+    } else {
+      const int k0 = kb + kt * BK;
+      a = OA::advance(A, p.lda, k0);
+      b = OB::advance(B, p.ldb, k0);
+    }
+  };
   auto issue = [&](int kt, uint4* la, uint4* lb) {
     const bf16_t *a, *b;
     if constexpr (KSEG > 1) {
@@ -248,6 +278,53 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 #pragma unroll
       for (int i = 0; i < TM; ++i) mma16(bq[set][j], af[set][i], acc[i][j], bf16_t{});
   };
+  constexpr int NLD = OA::PER_WAVE + OB::PER_WAVE;  // global->LDS loads per tile and wave
+  // One sub-step as MF slots in program order. Slot q issues MFMA q (set
+  // set_mma); the sub-step's NR fragment reads (k step ks_rd into set_rd: A
+  // fragments, then B) go one per slot from slot 0 at a stride of MF / NR;
+  // the DPS next-tile loads dq0.. go one per slot at a stride of MF / DPS,
+  // half a stride later.
+  constexpr int NR = TM + TN, DPS = (NLD + TPL_SLOT_DMA_SUBS - 1) / TPL_SLOT_DMA_SUBS;
+  auto slot_step = [&](int set_mma, const uint4* Ar, const uint4* Br, int ks_rd, int set_rd, int dq0,
+                       const bf16_t* na, const bf16_t* nb, uint4* la, uint4* lb) {
+#pragma unroll
+    for (int q = 0; q < MF; ++q) {
+      const int j = q / TM, i = q - (q / TM) * TM;
+      mma16(bq[set_mma][j], af[set_mma][i], acc[i][j], bf16_t{});
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if ((r * MF) / NR == q) {
+          if (r < TM) af[set_rd][r] = oa.frag(Ar, wm * WTM + r * 32, ks_rd, lane);
+          else bq[set_rd][r - TM] = ob.frag(Br, wn * WTN + (r - TM) * 32, ks_rd, lane);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < DPS; ++e) {
+        if ((e * MF) / DPS + MF / DPS / 2 == q) {
+          const int d = dq0 + e;
+          if (d < OA::PER_WAVE) oa.issue_one(na, la, wave, d);
+          else if (d < NLD) ob.issue_one(nb, lb, wave, d - OA::PER_WAVE);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // MFMAs of one sub-step with the next tile's loads dq0, dq0+1, ... placed
+  // one after every DMA_EVERY MFMAs.
+  auto mfmas_dma = [&](int set, int dq0, const bf16_t* na, const bf16_t* nb, uint4* la, uint4* lb) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        mma16(bq[set][j], af[set][i], acc[i][j], bf16_t{});
+        const int q = j * TM + i;
+        if ((q % TPL_DMA_EVERY) == TPL_DMA_EVERY - 1) {
+          const int d = dq0 + q / TPL_DMA_EVERY;
+          if (d < OA::PER_WAVE) oa.issue_one(na, la, wave, d);
+          else if (d < NLD) ob.issue_one(nb, lb, wave, d - OA::PER_WAVE);
+        }
+      }
+  };
   auto interleave = [&]() {
     if constexpr (FENCE) {
       sched_pairs<(NRD < MF ? NRD : MF), 0x100>();
@@ -263,6 +340,17 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   if (nk > 0) issue(0, sa0, sb0);
   wait_loads();
   __syncthreads();
+#if TPL_SLOTS && TPL_SLOT_EARLY
+  if (nk > 1) {
+    const bf16_t *na, *nb;
+    next_ptrs(1, na, nb);
+#pragma unroll
+    for (int d = 0; d < DPS; ++d) {
+      if (d < OA::PER_WAVE) oa.issue_one(na, sa1, wave, d);
+      else if (d < NLD) ob.issue_one(nb, sb1, wave, d - OA::PER_WAVE);
+    }
+  }
+#endif
   if (nk > 0) read_frags(sa0, sb0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const bool odd = kt & 1;
@@ -270,6 +358,53 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     const uint4* Bs = odd ? sb1 : sb0;
     uint4* An = odd ? sa0 : sa1;
     uint4* Bn = odd ? sb0 : sb1;
+#if TPL_SLOTS && TPL_SLOT_EARLY
+    // The first DPS loads of tile kt + 1 went out right after the previous
+    // barrier; sub-step 0 issues the rest. After this tile's barrier its own
+    // buffers are free (sub-step 3 fragments are in registers), so the first
+    // loads of tile kt + 2 go into them during sub-step 3.
+    const bf16_t *na, *nb;
+    next_ptrs(min(kt + 1, nk - 1), na, nb);
+    slot_step(0, As, Bs, 1, 1, DPS, na, nb, An, Bn);
+    slot_step(1, As, Bs, 2, 0, NLD, na, nb, An, Bn);
+    slot_step(0, As, Bs, 3, 1, NLD, na, nb, An, Bn);
+    wait_loads();
+    __syncthreads();
+    next_ptrs(min(kt + 2, nk - 1), na, nb);
+    // (near the end the clamped index repeats tile nk - 1 into a buffer no
+    // later fragment read uses; in bounds, drained after the loop)
+    slot_step(1, An, Bn, 0, 0, 0, na, nb, const_cast<uint4*>(As), const_cast<uint4*>(Bs));
+#elif TPL_SLOTS
+    const bf16_t *na, *nb;
+    next_ptrs(min(kt + 1, nk - 1), na, nb);
+    slot_step(0, As, Bs, 1, 1, 0, na, nb, An, Bn);          // sub-step 0, loads 0..
+    slot_step(1, As, Bs, 2, 0, DPS, na, nb, An, Bn);        // sub-step 1, loads DPS..
+    slot_step(0, As, Bs, 3, 1, 2 * DPS, na, nb, An, Bn);    // sub-step 2
+    wait_loads();
+    __syncthreads();
+    slot_step(1, An, Bn, 0, 0, NLD, na, nb, An, Bn);       // sub-step 3 + next tile's first reads
+#else
+#if TPL_DMA_SPREAD
+    constexpr int PER_SUB = MF / TPL_DMA_EVERY;  // loads per sub-step
+    const bf16_t *na, *nb;
+    next_ptrs(min(kt + 1, nk - 1), na, nb);
+    fence();
+    read_frags(As, Bs, 1, 1);  // sub-step 0: MFMAs on set 0, reads of sub-step 1, next tile's loads
+    mfmas_dma(0, 0, na, nb, An, Bn);
+    fence();
+    read_frags(As, Bs, 2, 0);  // sub-step 1
+    mfmas_dma(1, PER_SUB, na, nb, An, Bn);
+    if constexpr (2 * PER_SUB < NLD) {
+      fence();
+      read_frags(As, Bs, 3, 1);  // sub-step 2
+      mfmas_dma(0, 2 * PER_SUB, na, nb, An, Bn);
+    } else {
+      fence();
+      read_frags(As, Bs, 3, 1);  // sub-step 2
+      mfmas(0);
+      interleave();
+    }
+#else
     fence();
     read_frags(As, Bs, 1, 1);  // sub-step 0: MFMAs on set 0, reads of sub-step 1, next tile's loads
     mfmas(0);
@@ -283,6 +418,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     read_frags(As, Bs, 3, 1);  // sub-step 2
     mfmas(0);
     interleave();
+#endif
     fence();
     wait_loads();
     __syncthreads();
@@ -291,7 +427,11 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     read_frags(An, Bn, 0, 0);
     mfmas(1);
     interleave();
+#endif
   }
+#if TPL_SLOTS && TPL_SLOT_EARLY
+  wait_loads();
+#endif
   fence();
 
   if constexpr (EPI == EPI_SK_PART) {
@@ -330,7 +470,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED,
           bool FENCE = TPL_DIRECT_FENCE>
-__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256)))
 gemm_direct_kernel(const GemmArgs p) {
   TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
   direct_tile<Cfg, AK, BKM, EPI, TO, KSEG, SCHED, FENCE>(p, blockIdx.x, blockIdx.y, blockIdx.z, sa0, sb0, sa1, sb1);
@@ -342,7 +482,7 @@ gemm_direct_kernel(const GemmArgs p) {
 // and the tiles of a run share operand panels in that XCD's L2.
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, bool SCHED = TPL_DIRECT_SCHED,
           bool FENCE = TPL_DIRECT_FENCE>
-__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256)))
 gemm_sk_kernel(const GemmArgs p, const SkPlan s) {
   TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
   const int b = blockIdx.x;
@@ -413,7 +553,7 @@ struct GemmKind {
 // first, so the long tiles start first and the short ones fill in around
 // them (longest-processing-time order over the 256 CUs).
 template <class Cfg, class K0, class K1, int ROLE, bool SCHED = TPL_DIRECT_SCHED, bool FENCE = TPL_DIRECT_FENCE>
-__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256)))
 gemm_pair_kernel(const GemmArgs p0, const GemmArgs p1, int tiles0, int units0, int tiles1, int first1) {
   TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
   // blocks of the problem that goes first come first

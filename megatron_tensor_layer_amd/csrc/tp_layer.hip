@@ -154,7 +154,10 @@ Dims make_dims(long h, long a, long s, long b, long t, int dt) {
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Tile configurations.
-using CfgBig = TileCfg<bf16_t, 256, 256, 2, 2>;  // linear GEMMs
+#ifndef TPL_BIG_WN
+#define TPL_BIG_WN 2
+#endif
+using CfgBig = TileCfg<bf16_t, 256, 256, 2, TPL_BIG_WN>;  // linear GEMMs
 using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
 using CfgF32 = TileCfg<float, 64, 64, 2, 2>;     // fp32 configuration
 
