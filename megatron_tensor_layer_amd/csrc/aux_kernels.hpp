@@ -120,46 +120,78 @@ __global__ void __launch_bounds__(256) causal_softmax_long_kernel(const float* _
 
 // ---------------------------------------------------------------------------
 // D[z, q] = sum_c dC[q*b+beta, j*d+c] * C[q*b+beta, j*d+c],  z = beta*a_r + j.
-// Equals rowsum(P * dP) of the softmax backward because C = P V.
-// One thread per (token row, head).
+// Equals rowsum(P * dP) of the softmax backward because C = P V. C is read in
+// fp32 (the unrounded P V accumulator), so D matches the row sums of P * dP
+// that the dS epilogue subtracts it from.
+// One block per token row: the threads form the products of 4-element chunks
+// of the row (coalesced), park the chunk sums in LDS, and thread j then adds
+// head j's chunks in order. Heads are taken ROWDOT_LDS * 4 / d at a time.
 // ---------------------------------------------------------------------------
-// C is read in fp32 (the unrounded P V accumulator), so D matches the row
-// sums of P * dP that the dS epilogue subtracts it from.
+constexpr int ROWDOT_LDS = 4096;  // chunk sums per pass
 template <typename T>
 __global__ void __launch_bounds__(256) rowdot_kernel(const T* __restrict__ dC, const float* __restrict__ C,
-                                                     float* __restrict__ D, int Trows, int b, int ar, int d, int s) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)Trows * ar) return;
-  const int row = (int)(idx / ar), j = (int)(idx - (idx / ar) * ar);
+                                                     float* __restrict__ D, int b, int ar, int d, int s) {
+  __shared__ float part[ROWDOT_LDS];
+  const int row = blockIdx.x;
   const long ld = (long)ar * d;
-  const T* x = dC + row * ld + (long)j * d;
-  const float* y = C + row * ld + (long)j * d;
-  float acc = 0.0f;
-  for (int c = 0; c < d; c += 4) {
-    float u[4], v[4];
-    Elt<T>::load4(x + c, u);
-    Elt<float>::load4(y + c, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc += u[e] * v[e];
-  }
+  const T* x = dC + row * ld;
+  const float* y = C + row * ld;
+  const int cpd = d / 4;                     // chunks per head
+  const int hpp = ROWDOT_LDS / cpd;          // heads per pass
   const int sigma = row / b, beta = row - (row / b) * b;
-  D[((long)beta * ar + j) * s + sigma] = acc;
+  for (int h0 = 0; h0 < ar; h0 += hpp) {
+    const int nh = min(hpp, ar - h0);
+    const int nc = nh * cpd;
+    for (int c = threadIdx.x; c < nc; c += 256) {
+      float u[4], v[4];
+      Elt<T>::load4(x + (long)h0 * d + 4 * c, u);
+      Elt<float>::load4(y + (long)h0 * d + 4 * c, v);
+      part[c] = (u[0] * v[0] + u[1] * v[1]) + (u[2] * v[2] + u[3] * v[3]);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nh; j += 256) {
+      float acc = 0.0f;
+      for (int c = 0; c < cpd; ++c) acc += part[j * cpd + c];
+      D[((long)beta * ar + h0 + j) * s + sigma] = acc;
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
-// out[n] = sum_r X[r, n]: bias gradients. Block = 8 column threads (16 bytes
-// each) x 32 row groups; row groups are combined by a fixed LDS tree.
+// out[n] = sum_r X[r, n]: bias gradients, in two fixed-order passes.
+// colsum_part_kernel: block (column block x, row chunk y) = 8 column threads
+// (16 bytes each) x 32 row groups; each row group sums its rows of the chunk
+// (four loads in flight), the groups are combined by a fixed LDS tree, and
+// the chunk's fp32 sums go to part[y, n]. colsum_final_kernel adds the
+// chunks in order and rounds once.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) colsum_kernel(const T* __restrict__ X, T* __restrict__ out, int R, int N, long ld) {
+__global__ void __launch_bounds__(256) colsum_part_kernel(const T* __restrict__ X, float* __restrict__ part, int R,
+                                                          int N, long ld, int rows_per_chunk) {
   constexpr int VEC = Elt<T>::VEC;
   const int ct = threadIdx.x & 7, rg = threadIdx.x >> 3;
   const int col = (blockIdx.x * 8 + ct) * VEC;
+  const int r0 = blockIdx.y * rows_per_chunk, r1 = min(R, r0 + rows_per_chunk);
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
   if (col < N) {
-    for (int r = rg; r < R; r += 32) {
+    int r = r0 + rg;
+    for (; r + 96 < r1; r += 128) {
+      float v[4][VEC];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const T* p = X + (long)(r + 32 * u) * ld + col;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) Elt<T>::load4(p + e, &v[u][e]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += v[u][e];
+    }
+    for (; r < r1; r += 32) {
       const T* p = X + (long)r * ld + col;
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
@@ -182,12 +214,28 @@ __global__ void __launch_bounds__(256) colsum_kernel(const T* __restrict__ X, T*
     __syncthreads();
   }
   if (rg == 0 && col < N) {
+    float* dst = part + (long)blockIdx.y * N + col;
 #pragma unroll
     for (int e = 0; e < VEC; e += 4) {
       float v[4] = {red[0][ct * VEC + e], red[0][ct * VEC + e + 1], red[0][ct * VEC + e + 2], red[0][ct * VEC + e + 3]};
-      Elt<T>::store4(out + col + e, v);
+      Elt<float>::store4(dst + e, v);
     }
   }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_final_kernel(const float* __restrict__ part, T* __restrict__ out, int N,
+                                                           int chunks) {
+  const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (col >= N) return;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < chunks; ++z) {
+    float x[4];
+    Elt<float>::load4(part + (long)z * N + col, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += x[e];
+  }
+  Elt<T>::store4(out + col, v);
 }
 
 // ---------------------------------------------------------------------------
