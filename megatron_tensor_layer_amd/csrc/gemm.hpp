@@ -45,7 +45,7 @@ enum EpiKind : int {
   EPI_BIAS_SPLIT = 5,   // V = acc + bias[n] -> C (bf16); for n < c2_cols also the
                         // rounding residual V - bf16(V) -> C2 (bf16), same layout
   EPI_DUAL_F32 = 6,     // C = acc (storage type) and C2 = acc (fp32), same layout
-  EPI_SK_PART = 7       // fp32 accumulator fragment of a stream-K unit, in register order
+  EPI_SK_PART = 7       // fp32 accumulator fragment of a stream-K unit, tile-row-major
 };
 
 enum KMode : int {
@@ -272,65 +272,66 @@ __device__ __forceinline__ void mma16(const uint4& bfrag, const uint4& afrag, f3
 // epilogue on 4 consecutive columns of one row
 // ---------------------------------------------------------------------------
 
-template <int EPI, typename T, typename TO>
-__device__ __forceinline__ void epi_apply(const GemmArgs& p, int z1, int z2, int row, int col, float v[4], int split) {
+// V = 4 or 8 consecutive columns col..col+V-1 of one row (V divides N).
+template <int EPI, typename T, typename TO, int V = 4>
+__device__ __forceinline__ void epi_apply(const GemmArgs& p, int z1, int z2, int row, int col, float v[V], int split) {
   if constexpr (EPI == EPI_PARTIAL) {
-    Elt<float>::store4(p.part + ((long)split * p.M + row) * (long)p.N + col, v);
+    storev<float, V>(p.part + ((long)split * p.M + row) * (long)p.N + col, v);
     return;
   } else {
     if constexpr (EPI == EPI_LINEAR) {
       if (p.alpha != 1.0f) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] *= p.alpha;
+        for (int e = 0; e < V; ++e) v[e] *= p.alpha;
       }
       if (p.bias) {
-        float bb[4];
-        Elt<T>::load4(static_cast<const T*>(p.bias) + col, bb);
+        float bb[V];
+        loadv<T, V>(static_cast<const T*>(p.bias) + col, bb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += bb[e];
+        for (int e = 0; e < V; ++e) v[e] += bb[e];
       }
       if (p.resid) {
-        float rr[4];
-        Elt<T>::load4(static_cast<const T*>(p.resid) + (long)row * p.ldr + col, rr);
+        float rr[V];
+        loadv<T, V>(static_cast<const T*>(p.resid) + (long)row * p.ldr + col, rr);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += rr[e];
+        for (int e = 0; e < V; ++e) v[e] += rr[e];
       }
     } else if constexpr (EPI == EPI_BIAS_GELU) {
-      float bb[4];
-      Elt<T>::load4(static_cast<const T*>(p.bias) + col, bb);
-      float g[4];
+      float bb[V];
+      loadv<T, V>(static_cast<const T*>(p.bias) + col, bb);
+      float g[V];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < V; ++e) {
         v[e] += bb[e];
         g[e] = gelu_f(v[e]);
       }
-      Elt<T>::store4(static_cast<T*>(p.C2) + (long)row * p.ldc2 + col, g);
+      storev<T, V>(static_cast<T*>(p.C2) + (long)row * p.ldc2 + col, g);
     } else if constexpr (EPI == EPI_GELU_BWD) {
-      float u[4];
-      Elt<T>::load4(static_cast<const T*>(p.aux) + (long)row * p.ldx + col, u);
+      float u[V];
+      loadv<T, V>(static_cast<const T*>(p.aux) + (long)row * p.ldx + col, u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+      for (int e = 0; e < V; ++e) v[e] *= gelu_grad_f(u[e]);
     } else if constexpr (EPI == EPI_BIAS_SPLIT) {
-      float bb[4];
-      Elt<T>::load4(static_cast<const T*>(p.bias) + col, bb);
+      float bb[V];
+      loadv<T, V>(static_cast<const T*>(p.bias) + col, bb);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += bb[e];
+      for (int e = 0; e < V; ++e) v[e] += bb[e];
       if (col < p.c2_cols) {
-        float lo[4];
+        float lo[V];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
-        Elt<T>::store4(static_cast<T*>(p.C2) + (long)row * p.ldc + col, lo);
+        for (int e = 0; e < V; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
+        storev<T, V>(static_cast<T*>(p.C2) + (long)row * p.ldc + col, lo);
       }
     } else if constexpr (EPI == EPI_DUAL_F32) {
-      Elt<float>::store4(static_cast<float*>(p.C2) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
+      storev<float, V>(static_cast<float*>(p.C2) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
     } else if constexpr (EPI == EPI_SOFTMAX_BWD) {
-      float pp[4];
-      Elt<T>::load4(static_cast<const T*>(p.aux) + z1 * p.x_s1 + z2 * p.x_s2 + (long)row * p.ldx + col, pp);
+      float pp[V];
+      loadv<T, V>(static_cast<const T*>(p.aux) + z1 * p.x_s1 + z2 * p.x_s2 + (long)row * p.ldx + col, pp);
       const float D = p.rowv[z1 * p.r_s1 + z2 * p.r_s2 + row];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (col + e <= row) ? p.alpha * pp[e] * (v[e] - D) : 0.0f;
+      for (int e = 0; e < V; ++e) v[e] = (col + e <= row) ? p.alpha * pp[e] * (v[e] - D) : 0.0f;
     }
-    Elt<TO>::store4(static_cast<TO*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
+    storev<TO, V>(static_cast<TO*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
   }
 }
 

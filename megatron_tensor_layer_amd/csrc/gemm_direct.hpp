@@ -173,8 +173,8 @@ struct DirectOperand {
 
 // One output tile: linear tile index L (ordered by tile_coords), split-K
 // piece `split`, batch z. LDS buffers are passed in (two per operand).
-// EPI_SK_PART: K range [kb_, ke_) and the fragment goes to skdst in register
-// order (float4 index ((wave TM + i) TN + j) 4 + jj) 64 + lane).
+// EPI_SK_PART: K range [kb_, ke_) and the fp32 fragment goes to skdst as a
+// row-major BM x BN tile.
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int KSEG, bool SCHED, bool FENCE>
 __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split, int z, uint4* sa0, uint4* sb0,
                                             uint4* sa1, uint4* sb1, int kb_ = 0, int ke_ = 0,
@@ -434,39 +434,62 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 #endif
   fence();
 
-  if constexpr (EPI == EPI_SK_PART) {
-    float4* dst = reinterpret_cast<float4*>(skdst) + wave * (TM * TN * 256) + lane;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          dst[((i * TN + j) * 4 + jj) * 64] =
-              make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
-    return;
-  }
+  // Epilogue through LDS. Stored straight from the MFMA layout, a lane holds
+  // 4 columns of one row and a store instruction touches 32 rows, which
+  // serialises on the memory channel whenever the row pitch is a large power
+  // of two (every layer output). Instead the tile goes through LDS in TM
+  // passes: pass ps stages the 32-row block i = ps of every wave (fp32,
+  // 16-byte chunks XOR-swizzled by row), then each lane takes 8 consecutive
+  // columns of one row, so global loads and stores are 16-32 byte pieces of
+  // contiguous row segments.
+  constexpr int CH = BN / 4;          // 16-byte fp32 chunks per staged row
+  constexpr int C8 = BN / 8;          // 8-column chunks per row
+  constexpr int PR = Cfg::WM * 32;    // rows staged per pass
+  constexpr int PER = PR * C8 / NT;   // 8-column chunks per thread and pass
+  static_assert(CH >= 16 && (PR * C8) % NT == 0, "staging layout");
+  static_assert(PR * BN * 4 <= 2 * (BM + BN) * 128, "staging must fit the operand buffers");
+  __syncthreads();  // every wave is past its last fragment read and LDS load
+  float4* stage = reinterpret_cast<float4*>(sa0);
   const int r32 = lane & 31, g = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int row = m0 + wm * WTM + i * 32 + r32;
+  for (int ps = 0; ps < TM; ++ps) {
+    const int rl = wm * 32 + r32;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int col = n0 + wn * WTN + j * 32 + jj * 8 + g * 4;
-        float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
-        if (row < p.M && col < p.N) epi_apply<EPI, bf16_t, TO>(p, z1, z2, row, col, v, split);
+        const int ch = (wn * WTN + j * 32 + jj * 8) / 4 + g;
+        stage[rl * CH + (ch ^ (rl & 15))] =
+            make_float4(acc[ps][j][4 * jj], acc[ps][j][4 * jj + 1], acc[ps][j][4 * jj + 2], acc[ps][j][4 * jj + 3]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int c = tid + k * NT;
+      const int rs = c / C8, q = c - (c / C8) * C8;
+      const float4 x0 = stage[rs * CH + ((2 * q) ^ (rs & 15))];
+      const float4 x1 = stage[rs * CH + ((2 * q + 1) ^ (rs & 15))];
+      float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const int rt = (rs >> 5) * WTM + ps * 32 + (rs & 31);  // row within the tile
+      if constexpr (EPI == EPI_SK_PART) {
+        storev<float, 8>(skdst + rt * BN + 8 * q, v);  // the unit's fragment, tile-row-major
+      } else {
+        const int row = m0 + rt, col = n0 + 8 * q;
+        if (row < p.M && col < p.N) epi_apply<EPI, bf16_t, TO, 8>(p, z1, z2, row, col, v, split);
       }
     }
+    if (ps + 1 < TM) __syncthreads();
   }
 }
 
-#define TPL_DIRECT_LDS(BM, BN)                                 \
-  __shared__ __attribute__((aligned(1024))) uint4 sa0[BM * 8]; \
-  __shared__ __attribute__((aligned(1024))) uint4 sb0[BN * 8]; \
-  __shared__ __attribute__((aligned(1024))) uint4 sa1[BM * 8]; \
-  __shared__ __attribute__((aligned(1024))) uint4 sb1[BN * 8];
+// Two K-tile buffers per operand in one contiguous array (the epilogue
+// stages the output tile across them).
+#define TPL_DIRECT_LDS(BM, BN)                                              \
+  __shared__ __attribute__((aligned(1024))) uint4 lds_[2 * ((BM) + (BN)) * 8]; \
+  uint4* const sa0 = lds_;                                                  \
+  uint4* const sb0 = lds_ + (BM) * 8;                                       \
+  uint4* const sa1 = lds_ + ((BM) + (BN)) * 8;                              \
+  uint4* const sb1 = lds_ + (2 * (BM) + (BN)) * 8;
 
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED,
           bool FENCE = TPL_DIRECT_FENCE>
@@ -510,32 +533,28 @@ gemm_sk_kernel(const GemmArgs p, const SkPlan s) {
 }
 
 // Stream-K fix-up: for each tile of the stream-K region, the fixed-order sum
-// of its fragments, then the epilogue. One float4 of the tile per thread, in
-// the fragments' register order.
+// of its fragments (each stored tile-row-major), then the epilogue. Eight
+// consecutive columns of one row per thread.
 template <class Cfg, int EPI, typename TO, int ROLE>
 __global__ void __launch_bounds__(256) sk_fixup_kernel(const GemmArgs p, const SkPlan s) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, TM = Cfg::TM, TN = Cfg::TN;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, C8 = BN / 8;
   const int j = blockIdx.y;
-  const int q = blockIdx.x * 256 + threadIdx.x;  // float4 index within the tile
-  const int lane = q & 63, jj = (q >> 6) & 3;
-  int r = q >> 8;
-  const int jn = r % TN;
-  r /= TN;
-  const int i = r % TM, wave = r / TM;
-  const int wm = wave / Cfg::WN, wn = wave - (wave / Cfg::WN) * Cfg::WN;
+  const int q = blockIdx.x * 256 + threadIdx.x;  // 8-column chunk within the tile
+  const int rt = q / C8, ct = 8 * (q - (q / C8) * C8);
   int tm, tn;
   tile_coords(p, tm, tn, s.dp_tiles + j);
-  const int row = tm * BM + wm * Cfg::WTM + i * 32 + (lane & 31);
-  const int col = tn * BN + wn * Cfg::WTN + jn * 32 + jj * 8 + (lane >> 5) * 4;
-  if (row >= p.M || col >= p.N) return;
+  const int row = tm * BM + rt, col = tn * BN + ct;
+  if (rt >= BM || row >= p.M || col >= p.N) return;
   const int uf = (int)(((long)j * s.iters) / s.c), ul = (int)(((long)(j + 1) * s.iters - 1) / s.c);
-  const float4* src = reinterpret_cast<const float4*>(s.part + (long)j * s.f * (BM * BN)) + q;
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* src = s.part + (long)j * s.f * (BM * BN) + (long)rt * BN + ct;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k <= ul - uf; ++k) {
-    const float4 x = src[(long)k * (BM * BN / 4)];
-    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+    float x[8];
+    loadv<float, 8>(src + (long)k * (BM * BN), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += x[e];
   }
-  epi_apply<EPI, bf16_t, TO>(p, 0, 0, row, col, v, 0);
+  epi_apply<EPI, bf16_t, TO, 8>(p, 0, 0, row, col, v, 0);
 }
 
 // Operand layouts and epilogue of one problem of a grouped launch.

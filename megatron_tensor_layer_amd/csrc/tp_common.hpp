@@ -21,7 +21,7 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
-// Element traits: load / store 4 consecutive elements as fp32.
+// Element traits: load / store 4 (or 8) consecutive elements as fp32.
 template <typename T> struct Elt;
 
 template <> struct Elt<float> {
@@ -34,6 +34,8 @@ template <> struct Elt<float> {
     f32x4_t x = {v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4_t*>(p) = x;
   }
+  __device__ static __forceinline__ void load8(const float* p, float v[8]) { load4(p, v); load4(p + 4, v + 4); }
+  __device__ static __forceinline__ void store8(float* p, const float v[8]) { store4(p, v); store4(p + 4, v + 4); }
   __device__ static __forceinline__ float ld(const float* p) { return *p; }
   __device__ static __forceinline__ void st(float* p, float v) { *p = v; }
 };
@@ -50,6 +52,21 @@ template <> struct Elt<bf16_t> {
     bf16x4_t b = __builtin_convertvector(x, bf16x4_t);
     *reinterpret_cast<bf16x4_t*>(p) = b;
   }
+  __device__ static __forceinline__ void load8(const bf16_t* p, float v[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  }
+  __device__ static __forceinline__ void store8(bf16_t* p, const float v[8]) {
+    f32x4_t x = {v[0], v[1], v[2], v[3]}, y = {v[4], v[5], v[6], v[7]};
+    const bf16x4_t a = __builtin_convertvector(x, bf16x4_t), b = __builtin_convertvector(y, bf16x4_t);
+    const bf16x8_t c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    *reinterpret_cast<bf16x8_t*>(p) = c;
+  }
   __device__ static __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
   __device__ static __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
 };
@@ -60,6 +77,18 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
   const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
   const float pdf = 0.39894228040143268f * expf(-0.5f * x * x);
   return cdf + x * pdf;
+}
+
+// V consecutive elements (V = 4 or 8) as fp32.
+template <typename T, int V>
+__device__ __forceinline__ void loadv(const T* p, float v[V]) {
+  if constexpr (V == 8) Elt<T>::load8(p, v);
+  else Elt<T>::load4(p, v);
+}
+template <typename T, int V>
+__device__ __forceinline__ void storev(T* p, const float v[V]) {
+  if constexpr (V == 8) Elt<T>::store8(p, v);
+  else Elt<T>::store4(p, v);
 }
 
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -209,7 +209,7 @@ SavedLayout saved_layout(const Dims& D, int blk) {
 // ~5 TB/s plus a launch gap for the fix-up.
 SkPlan sk_plan(long M, long N, long K) {
   SkPlan s{};
-  if (K % CfgBig::BK != 0) return s;
+  if (K % CfgBig::BK != 0 || N % 8 != 0) return s;
   const long tiles = cdivl(M, CfgBig::BM) * cdivl(N, CfgBig::BN);
   const long I = K / CfgBig::BK;
   const long W = tiles / 256, R = tiles % 256;
@@ -336,6 +336,13 @@ bool ragged_k(const GemmArgs& p, int kseg) {
   return p.K % Cfg::BK != 0;
 }
 
+// The direct kernel needs whole K tiles and writes its epilogue in 8-column
+// pieces (N, ldc and the other column strides multiples of 8).
+template <class Cfg>
+bool direct_ok(const GemmArgs& p, int kseg) {
+  return !ragged_k<Cfg>(p, kseg) && p.N % 8 == 0;
+}
+
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1>
 hipError_t launch(GemmArgs p, int batch, hipStream_t st) {
   p.tiles_m = cdiv(p.M, Cfg::BM);
@@ -352,7 +359,7 @@ hipError_t launch(GemmArgs p, int batch, hipStream_t st) {
       const dim3 grid(tiles, p.splits, 1);
       bool done = false;
       if constexpr (BF) {
-        if (!ragged_k<Cfg>(p, 1)) {
+        if (direct_ok<Cfg>(p, 1)) {
           hipLaunchKernelGGL((gemm_direct_kernel<Cfg, AK, BKM, EPI_PARTIAL, float, ROLE, 1>), grid, dim3(Cfg::NT), 0,
                              st, p);
           done = true;
@@ -373,7 +380,7 @@ hipError_t launch(GemmArgs p, int batch, hipStream_t st) {
   }
   const dim3 grid(tiles, 1, batch);
   if constexpr (BF) {
-    if (!ragged_k<Cfg>(p, KSEG)) {
+    if (direct_ok<Cfg>(p, KSEG)) {
       hipLaunchKernelGGL((gemm_direct_kernel<Cfg, AK, BKM, EPI, TO, ROLE, KSEG>), grid, dim3(Cfg::NT), 0, st, p);
       return hipGetLastError();
     }
@@ -437,7 +444,7 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
       hipLaunchKernelGGL((gemm_sk_kernel<CfgBig, AK, BKM, EPI, bf16_t, ROLE>), dim3(s.dp_tiles + s.units),
                          dim3(CfgBig::NT), 0, st, p, s);
       hipLaunchKernelGGL((sk_fixup_kernel<CfgBig, EPI, bf16_t, ROLE>),
-                         dim3(CfgBig::BM * CfgBig::BN / 4 / 256, s.sk_tiles), dim3(256), 0, st, p, s);
+                         dim3(CfgBig::BM * CfgBig::BN / 8 / 256, s.sk_tiles), dim3(256), 0, st, p, s);
       return hipGetLastError();
     }
     p.splits = choose_splits(p.M, p.N, p.K);
@@ -453,7 +460,7 @@ template <int E0, int ROLE, int ROLE0, int ROLE1>
 hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_t st) {
   using K0 = GemmKind<true, true, E0, bf16_t>;
   using K1 = GemmKind<false, false, EPI_LINEAR, bf16_t>;
-  const bool direct = D.dt == TP_BF16 && !ragged_k<CfgBig>(p0, 1) && !ragged_k<CfgBig>(p1, 1);
+  const bool direct = D.dt == TP_BF16 && direct_ok<CfgBig>(p0, 1) && direct_ok<CfgBig>(p1, 1);
   if (!direct) {
     TRY_E((linear<true, true, E0, ROLE0>(D, p0, part, st)));
     return linear<false, false, EPI_LINEAR, ROLE1>(D, p1, part, st);
