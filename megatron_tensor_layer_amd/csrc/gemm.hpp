@@ -43,7 +43,7 @@ enum EpiKind : int {
   EPI_SOFTMAX_BWD = 3,  // C = (n <= m) ? alpha * aux[m,n] * (acc - rowv[m]) : 0
   EPI_PARTIAL = 4,      // split-K: fp32 partial[split, m, n] = acc
   EPI_BIAS_SPLIT = 5,   // V = acc + bias[n] -> C (bf16); for n < c2_cols also the
-                        // rounding residual V - bf16(V) -> C2 (bf16), same layout
+                        // rounding residual V - bf16(V) -> C2 (bf16, row pitch ldc2)
   EPI_DUAL_F32 = 6,     // C = acc (storage type) and C2 = acc (fp32), same layout
   EPI_SK_PART = 7       // fp32 accumulator fragment of a stream-K unit, tile-row-major
 };
@@ -320,7 +320,7 @@ __device__ __forceinline__ void epi_apply(const GemmArgs& p, int z1, int z2, int
         float lo[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
-        storev<T, V>(static_cast<T*>(p.C2) + (long)row * p.ldc + col, lo);
+        storev<T, V>(static_cast<T*>(p.C2) + (long)row * p.ldc2 + col, lo);
       }
     } else if constexpr (EPI == EPI_DUAL_F32) {
       storev<float, V>(static_cast<float*>(p.C2) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);

@@ -37,6 +37,7 @@
 #include "../../include/tp_layer.h"
 #include "aux_kernels.hpp"
 #include "gemm.hpp"
+#include "flash_attn.hpp"
 #include "gemm_direct.hpp"
 
 using namespace tpl;
@@ -59,7 +60,7 @@ enum Role : int {
   R_FC2_DGRAD, R_FC2_WGRAD, R_DB2, R_FC1_DGRAD, R_FC1_WGRAD, R_DB1,
   R_O_DGRAD, R_O_WGRAD, R_DBO, R_ROWDOT, R_DS, R_DV, R_DQ, R_DK,
   R_QKV_DGRAD, R_QKV_WGRAD, R_DBQKV, R_REDUCE, R_GEMM,
-  R_FC2_BWD, R_FC1_BWD, R_O_BWD, R_QKV_BWD, R_COUNT
+  R_FC2_BWD, R_FC1_BWD, R_O_BWD, R_QKV_BWD, R_ATT_FWD, R_ATT_DKV, R_ATT_DQ, R_COUNT
 };
 
 const char* const kRoleName[R_COUNT] = {
@@ -67,7 +68,8 @@ const char* const kRoleName[R_COUNT] = {
   "fc2_dgrad", "fc2_wgrad", "db2", "fc1_dgrad", "fc1_wgrad", "db1",
   "o_dgrad", "o_wgrad", "dbo", "rowdot", "ds", "dv", "dq", "dk",
   "qkv_dgrad", "qkv_wgrad", "dbqkv", "reduce", "gemm",
-  "fc2_dgrad+wgrad", "fc1_dgrad+wgrad", "o_dgrad+wgrad", "qkv_dgrad+wgrad"};
+  "fc2_dgrad+wgrad", "fc1_dgrad+wgrad", "o_dgrad+wgrad", "qkv_dgrad+wgrad",
+  "attn_fwd", "attn_dkv", "attn_dq"};
 
 namespace prof {
 struct Rec {
@@ -176,15 +178,48 @@ int choose_splits(long M, long N, long K) {
 // of the attention tile in every row; all causal GEMMs use this tile.
 int att_tile(int dt) { return dt == TP_BF16 ? CfgMid::BM : CfgF32::BM; }
 
+// The bf16 path runs attention as fused flash kernels (flash_attn.hpp) for
+// the head widths they are built for; other widths and the fp32
+// configuration materialise the causal s x s matrices with the GEMM kernels.
+bool flash(const Dims& D) {
+  if (D.dt != TP_BF16) return false;
+  if (D.d != 64 && D.d != 96 && D.d != 128 && D.d != 160) return false;
+  return (double)D.T * D.q3 * 2.0 < 4294967296.0;  // 32-bit byte offsets of the tile loads
+}
+
+// Flash attention chunk size: when the heads' query
+// blocks alone keep the CUs busy, blocks run whole; otherwise their tile
+// ranges are cut into chunks of 8 tiles (the causal ranges differ up to s /
+// 64 : 1 in length) and merged by a combine kernel.
+int fa_chunk_tiles(const Dims& D) {
+  const long nblk = cdivl(D.s, fa::BQ), ntot = cdivl(D.s, fa::BT);
+  if (D.z * nblk >= 4 * 256) return (int)(ntot + (ntot & 1));
+  return 8;
+}
+// fp32 partials of split blocks: forward C (+ m, l per row) or backward dK, dV
+// (the dQ partials reuse the region after the dK/dV combine).
+size_t fa_part_bytes(const Dims& D, int blk) {
+  const int ct = fa_chunk_tiles(D);
+  const size_t slots = (size_t)fa::part_slot((int)D.z, 0, 0, (int)D.s, ct, 1);  // z x blocks x chunks x 128
+  return blk == TP_ATTN ? 4 * slots * std::max<long>(D.d + 2, 2 * D.d) : 0;
+}
+
 // ATTN keeps QKV, P and C (and, for bf16, C in fp32 for the softmax
-// backward's row term); MLP keeps U and Z.
+// backward's row term), or with the flash kernels QKV, the Q/K residuals,
+// C (bf16 and fp32) and the per-query log-sum-exp; MLP keeps U and Z.
 struct SavedLayout {
-  size_t qkv, p, c, c32, u, z, total;
+  size_t qkv, qkv_lo, lse, p, c, c32, u, z, total;
 };
 SavedLayout saved_layout(const Dims& D, int blk) {
   SavedLayout L{};
   size_t o = 0;
-  if (blk == TP_ATTN) {
+  if (blk == TP_ATTN && flash(D)) {  // QKV, the Q/K rounding residuals, C (bf16, fp32), LSE
+    L.qkv = o;    o = al(o + (size_t)D.T * D.q3 * D.es);
+    L.qkv_lo = o; o = al(o + (size_t)D.T * 2 * D.hr * D.es);
+    L.c = o;      o = al(o + (size_t)D.T * D.hr * D.es);
+    L.c32 = o;    o = al(o + (size_t)D.T * D.hr * 4);
+    L.lse = o;    o = al(o + (size_t)D.z * D.s * 4);
+  } else if (blk == TP_ATTN) {
     L.qkv = o; o = al(o + (size_t)D.T * D.q3 * D.es);
     L.p = o;   o = al(o + (size_t)D.z * D.s * D.s * D.es);
     L.c = o;   o = al(o + (size_t)D.T * D.hr * D.es);
@@ -294,18 +329,21 @@ WsLayout ws_layout(const Dims& D, int blk) {
     upd(M1, N1, K1);
     pb = std::max(pb, pair_partial_bytes(D, M0, N0, K0, M1, N1, K1));
   };
-  // column sums of the backward pass share the partials region
+  // column sums of the backward pass share the partials region, and so do
+  // the flash attention chunks (every user runs in turn on the stream)
   pb = std::max(pb, colsum_bytes(D.T, blk == TP_ATTN ? std::max(D.h, D.q3) : std::max(D.h, D.fr)));
+  if (flash(D)) pb = std::max(pb, al(fa_part_bytes(D, blk)));
   if (blk == TP_ATTN) {
     upd(D.T, D.q3, D.h); upd(D.T, D.h, D.hr);
     upd2(D.T, D.hr, D.h, D.hr, D.h, D.T); upd2(D.T, D.h, D.q3, D.h, D.q3, D.T);
-    size_t fwd = al((size_t)D.z * D.s * D.s * 4);
+    const bool fl = flash(D);
+    size_t fwd = fl ? 0 : al((size_t)D.z * D.s * D.s * 4);
     W.qkv_lo = fwd;
-    if (D.dt == TP_BF16) fwd = al(fwd + (size_t)D.T * D.q3 * D.es);
+    if (D.dt == TP_BF16 && !fl) fwd = al(fwd + (size_t)D.T * D.q3 * D.es);
     size_t o = 0;
     W.dc = o;   o = al(o + (size_t)D.T * D.hr * D.es);
     W.D = o;    o = al(o + (size_t)D.z * D.s * 4);
-    W.ds = o;   o = al(o + (size_t)D.z * D.s * D.s * D.es);
+    W.ds = o;   if (!fl) o = al(o + (size_t)D.z * D.s * D.s * D.es);
     W.dqkv = o; o = al(o + (size_t)D.T * D.q3 * D.es);
     W.s = 0;
     W.part = std::max(fwd, o);
@@ -557,6 +595,58 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 double att_flops(const Dims& D) { return 2.0 * D.z * D.s * D.s * D.d; }
 double tri_elems(const Dims& D) { return (double)D.z * D.s * (D.s + 1) / 2.0; }
 
+// Flash attention launches (256 threads): the main kernels on a 1-D grid of
+// z * items workgroups, the combines on (blocks * d / 8, z).
+FaArgs fa_args(const Dims& D) {
+  FaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.s = (int)D.s; a.b = (int)D.b; a.ar = (int)D.ar; a.d = (int)D.d; a.hr = (int)D.hr; a.q3 = (int)D.q3;
+  a.z = (int)D.z;
+  a.ct = fa_chunk_tiles(D);
+  a.sc = (float)(1.0 / std::sqrt((double)D.d));
+  a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D.d));  // log2(e) / sqrt(d)
+  return a;
+}
+
+#define TPL_FA_SWITCH(KERNEL_D, GRID)                                                         \
+  do {                                                                                        \
+    switch (D.d) {                                                                            \
+      case 64: hipLaunchKernelGGL(KERNEL_D(64), GRID, dim3(256), 0, st, a); break;            \
+      case 96: hipLaunchKernelGGL(KERNEL_D(96), GRID, dim3(256), 0, st, a); break;            \
+      case 128: hipLaunchKernelGGL(KERNEL_D(128), GRID, dim3(256), 0, st, a); break;          \
+      case 160: hipLaunchKernelGGL(KERNEL_D(160), GRID, dim3(256), 0, st, a); break;          \
+      default: return hipErrorInvalidValue;                                                   \
+    }                                                                                         \
+  } while (0)
+#define TPL_FA_FWD(DD) fa_fwd_kernel<DD>
+#define TPL_FA_FWD_COMBINE(DD) fa_fwd_combine_kernel<DD>
+#define TPL_FA_DKV(DD) fa_bwd_dkv_kernel<DD>
+#define TPL_FA_DQ(DD) fa_bwd_dq_kernel<DD>
+#define TPL_FA_KV_COMBINE(DD) (fa_bwd_combine_kernel<DD, true>)
+#define TPL_FA_Q_COMBINE(DD) (fa_bwd_combine_kernel<DD, false>)
+
+bool fa_split(const Dims& D, const FaArgs& a) { return a.ct < cdivl(D.s, fa::BT); }
+dim3 fa_combine_grid(const Dims& D) { return dim3((unsigned)(cdivl(D.s, fa::BQ) * (D.d / 8)), (unsigned)D.z); }
+
+hipError_t fa_fwd(const Dims& D, FaArgs a, hipStream_t st) {
+  a.items = fa::items_per_head(a.s, a.ct, false);
+  TPL_FA_SWITCH(TPL_FA_FWD, dim3((unsigned)(a.z * a.items)));
+  if (fa_split(D, a)) TPL_FA_SWITCH(TPL_FA_FWD_COMBINE, fa_combine_grid(D));
+  return hipGetLastError();
+}
+hipError_t fa_dkv(const Dims& D, FaArgs a, hipStream_t st) {
+  a.items = fa::items_per_head(a.s, a.ct, true);
+  TPL_FA_SWITCH(TPL_FA_DKV, dim3((unsigned)(a.z * a.items)));
+  if (fa_split(D, a)) TPL_FA_SWITCH(TPL_FA_KV_COMBINE, fa_combine_grid(D));
+  return hipGetLastError();
+}
+hipError_t fa_dq(const Dims& D, FaArgs a, hipStream_t st) {
+  a.items = fa::items_per_head(a.s, a.ct, false);
+  TPL_FA_SWITCH(TPL_FA_DQ, dim3((unsigned)(a.z * a.items)));
+  if (fa_split(D, a)) TPL_FA_SWITCH(TPL_FA_Q_COMBINE, fa_combine_grid(D));
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // attention block
 // ---------------------------------------------------------------------------
@@ -573,7 +663,7 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
   void* qkv_lo = B8(ws, W.qkv_lo);
   float* part = reinterpret_cast<float*>(B8(ws, W.part));
   const double es = (double)D.es, sde = (double)D.z * D.s * D.d * es;
-  const bool bf = D.dt == TP_BF16;
+  const bool bf = D.dt == TP_BF16, fl = flash(D);
 
   {  // QKV_r = X Wqkv_r + b_qkv_r; bf16 also keeps the rounding residual of Q and K
     GemmArgs p = gargs(D.T, D.q3, D.h);
@@ -582,12 +672,26 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
     p.C = qkv; p.ldc = D.q3;
     p.bias = w->b_in;
     if (bf) {
-      p.C2 = qkv_lo; p.c2_cols = (int)(2 * D.hr);
+      // flash: residuals saved for the backward, [T, 2 h/t]; else workspace, row pitch 3h/t
+      p.C2 = fl ? B8(saved, S.qkv_lo) : qkv_lo;
+      p.ldc2 = fl ? 2 * D.hr : D.q3;
+      p.c2_cols = (int)(2 * D.hr);
       TRY((linear<true, false, EPI_BIAS_SPLIT, R_QKV_FWD>(D, p, part, st)));
     } else {
       TRY((linear<true, false, EPI_LINEAR, R_QKV_FWD>(D, p, part, st)));
     }
   }
+  if (fl) {  // C = causal softmax(Q K^T / sqrt(d)) V in one pass, online softmax; LSE saved
+    prof::Scope sc(R_ATT_FWD, 2.0 * att_flops(D), 8.0 * sde + 4.0 * D.z * D.s, st);
+    FaArgs a = fa_args(D);
+    a.qkv = static_cast<const bf16_t*>(qkv);
+    a.qkv_lo = reinterpret_cast<const bf16_t*>(B8(saved, S.qkv_lo));
+    a.ctx = static_cast<bf16_t*>(C);
+    a.ctx32 = static_cast<float*>(C32);
+    a.lse = reinterpret_cast<float*>(B8(saved, S.lse));
+    a.part = part;
+    TRY(fa_fwd(D, a, st));
+  } else {
   {  // S_z = Q_z K_z^T / sqrt(d), lower-triangular tiles, fp32.
      // bf16: Q = Qh + Ql, K = Kh + Kl (Ql, Kl the bf16 rounding residuals);
      // S = Qh Kh^T + Qh Kl^T + Ql Kh^T in one K-segmented MFMA pass, which
@@ -629,6 +733,7 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
       TRY((run<true, false, EPI_LINEAR, R_PV, KIND_MID>(D, p, (int)D.z, st)));
     }
   }
+  }  // materialised attention
   {  // partial = C Wo_r
     GemmArgs p = gargs(D.T, D.h, D.hr);
     p.A = C; p.lda = D.hr;
@@ -673,6 +778,24 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     if (D.dt == TP_BF16) TRY(rowdot_t<bf16_t>(D, dC, C32, Dv, st));
     else TRY(rowdot_t<float>(D, dC, C32, Dv, st));
   }
+  if (flash(D)) {  // dK, dV per key block; dQ per query block (P and dP recomputed)
+    FaArgs a = fa_args(D);
+    a.qkv = static_cast<const bf16_t*>(qkv);
+    a.qkv_lo = reinterpret_cast<const bf16_t*>(B8(saved, S.qkv_lo));
+    a.lse = const_cast<float*>(reinterpret_cast<const float*>(B8(saved, S.lse)));
+    a.dctx = static_cast<const bf16_t*>(dC);
+    a.dsum = Dv;
+    a.dqkv = static_cast<bf16_t*>(dqkv);
+    a.part = part;
+    {
+      prof::Scope sc(R_ATT_DKV, 3.0 * att_flops(D), 8.0 * sde + 8.0 * D.z * D.s, st);
+      TRY(fa_dkv(D, a, st));
+    }
+    {
+      prof::Scope sc(R_ATT_DQ, att_flops(D), 7.0 * sde + 8.0 * D.z * D.s, st);
+      TRY(fa_dq(D, a, st));
+    }
+  } else {
   {  // dS = P * (dC V^T - D) / sqrt(d), lower-triangular tiles
     prof::Scope sc(R_DS, att_flops(D), 2 * sde + 2 * es * tri_elems(D) + 4.0 * D.z * D.s, st);
     GemmArgs p = gargs(D.s, D.s, D.d);
@@ -716,6 +839,7 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     p.kmode = K_UPPER;
     TRY((run<false, false, EPI_LINEAR, R_DK, KIND_MID>(D, p, (int)D.z, st)));
   }
+  }  // materialised attention
   {  // dX_r = dQKV Wqkv_r^T
     GemmArgs p = gargs(D.T, D.h, D.q3);
     p.A = dqkv; p.lda = D.q3;

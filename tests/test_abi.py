@@ -57,12 +57,23 @@ def test_check_args(args, expect):
 
 def test_saved_and_workspace_sizes():
     h, a, s, b, t = 12288, 96, 2048, 1, 8
-    T, ar = s * b, a // t
+    T, ar, hr = s * b, a // t, h // t
+    # bf16 with d = 128 runs the fused flash kernels: the attention block keeps
+    # QKV, the Q/K rounding residuals, C in bf16 and fp32 and one log-sum-exp
+    # per query, and neither it nor its workspace holds any s x s matrix
     sa = tp.tp_saved_bytes(h, a, s, b, t, tp.TP_BF16, tp.TP_ATTN)
+    assert sa >= 2 * (T * 3 * hr + T * 2 * hr + T * hr) + 4 * T * hr + 4 * b * ar * s
+    assert sa < 2 * b * ar * s * s
+    assert tp.tp_workspace_bytes(h, a, s, b, t, tp.TP_BF16, tp.TP_ATTN) < 4 * b * ar * s * s  # no fp32 scores
     sm = tp.tp_saved_bytes(h, a, s, b, t, tp.TP_BF16, tp.TP_MLP)
-    assert sa >= 2 * (T * 3 * h // t + b * ar * s * s + T * h // t)
     assert sm >= 2 * 2 * T * 4 * h // t
-    assert tp.tp_workspace_bytes(h, a, s, b, t, tp.TP_BF16, tp.TP_ATTN) >= 4 * b * ar * s * s
+    # fp32, and bf16 with a head width the flash kernels are not built for
+    # (d = 48), materialise P (saved) and the fp32 scores (workspace)
+    for dt, es, a2 in ((tp.TP_FP32, 4, a), (tp.TP_BF16, 2, 256)):
+        ar2 = a2 // t
+        sa2 = tp.tp_saved_bytes(h, a2, s, b, t, dt, tp.TP_ATTN)
+        assert sa2 >= es * (T * 3 * hr + b * ar2 * s * s + T * hr)
+        assert tp.tp_workspace_bytes(h, a2, s, b, t, dt, tp.TP_ATTN) >= 4 * b * ar2 * s * s
     assert tp.tp_saved_bytes(h, a, s, b, 5, tp.TP_BF16, tp.TP_ATTN) == 0  # a % t != 0 -> 0
 
 

@@ -105,7 +105,22 @@ SMALL = {
     "bf16_splitk": I.make_config("bf16_splitk", h=2048, a=16, s=256, b=1, t=2, dtype="bf16"),
     # fp32, ragged and several tiles
     "fp32_ragged": I.make_config("fp32_ragged", h=128, a=8, s=80, b=3, t=2, dtype="fp32"),
+    # bf16, d = 128, sequence long enough (18 key tiles of 64) that the fused
+    # attention cuts the longer causal ranges into chunks and merges them
+    "bf16_chunked": I.make_config("bf16_chunked", h=256, a=2, s=1152, b=1, t=2, dtype="bf16"),
+    # bf16 with a head width the fused attention kernels are not built for
+    # (d = 48): attention through the materialised s x s GEMM path
+    "bf16_d48": I.make_config("bf16_d48", h=192, a=4, s=96, b=2, t=2, dtype="bf16"),
 }
+
+# bf16 head widths that run the fused (flash) attention kernels
+FLASH_D = (64, 96, 128, 160)
+
+
+def attention_roles(cfg):
+    if cfg.dtype == "bf16" and cfg.d in FLASH_D:
+        return {"attn_fwd", "attn_dkv", "attn_dq"}
+    return {"scores", "softmax", "pv", "ds", "dv", "dq", "dk"}
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -290,14 +305,18 @@ def test_reduce_with_bias_and_residual_matches_block_output(dtype):
     assert rel_err(to_np(out), ref) <= (4e-3 if dtype == "bf16" else 1e-6)
 
 
-def test_profiler_attributes_every_role():
-    cfg = SMALL["bf16_ragged"]
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_d48"])
+def test_profiler_attributes_every_role(name):
+    cfg = SMALL[name]
     tp.tp_prof_enable(True)
     full_layer_gpu(cfg)
     tp.tp_prof_enable(False)
     prof = tp.tp_prof_read()
-    roles = {"qkv_fwd", "scores", "softmax", "pv", "o_fwd", "fc1_fwd", "fc2_fwd", "db2", "db1", "dbo", "rowdot",
-             "ds", "dv", "dq", "dk", "dbqkv", "reduce"}
+    roles = {"qkv_fwd", "o_fwd", "fc1_fwd", "fc2_fwd", "db2", "db1", "dbo", "rowdot", "dbqkv", "reduce"}
+    roles |= attention_roles(cfg)
+    # the fused and the materialised attention never both run
+    other = {"attn_fwd", "attn_dkv", "attn_dq", "scores", "softmax", "pv", "ds", "dv", "dq", "dk"} - roles
+    assert not (other & set(prof)), other & set(prof)
     # a weight's input- and weight-gradient GEMMs run as one grouped launch
     # when both take whole 64-deep K steps, else as two launches
     for w in ("fc2", "fc1", "o", "qkv"):
