@@ -159,39 +159,38 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const T* __restrict__ dC, c
 }
 
 // ---------------------------------------------------------------------------
-// out[n] = sum_r X[r, n]: bias gradients, in two fixed-order passes.
-// colsum_part_kernel: block (column block x, row chunk y) = 8 column threads
-// (16 bytes each) x 32 row groups; each row group sums its rows of the chunk
-// (four loads in flight), the groups are combined by a fixed LDS tree, and
-// the chunk's fp32 sums go to part[y, n]. colsum_final_kernel adds the
-// chunks in order and rounds once.
+// out[n] = sum_r X[r, n]: bias gradients in one fixed-order pass. A block owns
+// 8 x VEC columns (8 column threads of 16 bytes: a 128-byte row piece) over all
+// R rows. Its 32 row groups each sum rows rg, rg + 32, ... with 16 loads in
+// flight per thread (64 KB per block, enough to cover HBM latency with one
+// block per CU), then a fixed LDS tree adds the groups and the result is
+// rounded once.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) colsum_part_kernel(const T* __restrict__ X, float* __restrict__ part, int R,
-                                                          int N, long ld, int rows_per_chunk) {
-  constexpr int VEC = Elt<T>::VEC;
-  const int ct = threadIdx.x & 7, rg = threadIdx.x >> 3;
-  const int col = (blockIdx.x * 8 + ct) * VEC;
-  const int r0 = blockIdx.y * rows_per_chunk, r1 = min(R, r0 + rows_per_chunk);
+__global__ void __launch_bounds__(256) colsum_kernel(const T* __restrict__ X, T* __restrict__ out, int R, int N,
+                                                     long ld) {
+  constexpr int VEC = Elt<T>::VEC, CT = 8, RG = 256 / CT, W = CT * VEC, U = 16;
+  const int ct = threadIdx.x % CT, rg = threadIdx.x / CT;
+  const int col = (blockIdx.x * CT + ct) * VEC;
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
   if (col < N) {
-    int r = r0 + rg;
-    for (; r + 96 < r1; r += 128) {
-      float v[4][VEC];
+    int r = rg;
+    for (; r + (U - 1) * RG < R; r += U * RG) {
+      uint4 v[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const T* p = X + (long)(r + 32 * u) * ld + col;
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint4*>(X + (long)(r + RG * u) * ld + col);
 #pragma unroll
-        for (int e = 0; e < VEC; e += 4) Elt<T>::load4(p + e, &v[u][e]);
+      for (int u = 0; u < U; ++u) {
+        float f[VEC];
+        Elt<T>::load4(reinterpret_cast<const T*>(&v[u]), f);
+        if constexpr (VEC == 8) Elt<T>::load4(reinterpret_cast<const T*>(&v[u]) + 4, f + 4);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += f[e];
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += v[u][e];
     }
-    for (; r < r1; r += 32) {
+    for (; r < R; r += RG) {
       const T* p = X + (long)r * ld + col;
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
@@ -202,40 +201,18 @@ __global__ void __launch_bounds__(256) colsum_part_kernel(const T* __restrict__ 
       }
     }
   }
-  __shared__ float red[32][8 * VEC + 1];
+  __shared__ float red[RG][W + 1];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) red[rg][ct * VEC + e] = acc[e];
   __syncthreads();
-  for (int w = 16; w > 0; w >>= 1) {
-    if (rg < w) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) red[rg][ct * VEC + e] += red[rg + w][ct * VEC + e];
-    }
+  for (int h = RG / 2; h >= 1; h /= 2) {  // fixed tree over the row groups
+    for (int i = threadIdx.x; i < h * W; i += 256) red[i / W][i % W] += red[i / W + h][i % W];
     __syncthreads();
   }
-  if (rg == 0 && col < N) {
-    float* dst = part + (long)blockIdx.y * N + col;
-#pragma unroll
-    for (int e = 0; e < VEC; e += 4) {
-      float v[4] = {red[0][ct * VEC + e], red[0][ct * VEC + e + 1], red[0][ct * VEC + e + 2], red[0][ct * VEC + e + 3]};
-      Elt<float>::store4(dst + e, v);
-    }
+  if (threadIdx.x < W) {
+    const int c = blockIdx.x * W + threadIdx.x;
+    if (c < N) Elt<T>::st(out + c, red[0][threadIdx.x]);
   }
-}
-
-template <typename T>
-__global__ void __launch_bounds__(256) colsum_final_kernel(const float* __restrict__ part, T* __restrict__ out, int N,
-                                                           int chunks) {
-  const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (col >= N) return;
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < chunks; ++z) {
-    float x[4];
-    Elt<float>::load4(part + (long)z * N + col, x);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] += x[e];
-  }
-  Elt<T>::store4(out + col, v);
 }
 
 // ---------------------------------------------------------------------------

@@ -270,10 +270,6 @@ SkPlan sk_plan(long M, long N, long K) {
   return s;
 }
 
-// Bias-gradient column sums: rows per chunk and chunk count.
-constexpr int COLSUM_ROWS = 128;
-long colsum_chunks(long R) { return std::max(1L, cdivl(R, COLSUM_ROWS)); }
-size_t colsum_bytes(long R, long N) { return al((size_t)colsum_chunks(R) * N * 4); }
 
 size_t partial_bytes(const Dims& D, long M, long N, long K) {
   if (D.dt != TP_BF16) return 0;
@@ -329,9 +325,8 @@ WsLayout ws_layout(const Dims& D, int blk) {
     upd(M1, N1, K1);
     pb = std::max(pb, pair_partial_bytes(D, M0, N0, K0, M1, N1, K1));
   };
-  // column sums of the backward pass share the partials region, and so do
-  // the flash attention chunks (every user runs in turn on the stream)
-  pb = std::max(pb, colsum_bytes(D.T, blk == TP_ATTN ? std::max(D.h, D.q3) : std::max(D.h, D.fr)));
+  // the flash attention chunks share the partials region (every user runs in
+  // turn on the stream)
   if (flash(D)) pb = std::max(pb, al(fa_part_bytes(D, blk)));
   if (blk == TP_ATTN) {
     upd(D.T, D.q3, D.h); upd(D.T, D.h, D.hr);
@@ -538,24 +533,16 @@ hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_
   return hipGetLastError();
 }
 
-// Column sums in row chunks of COLSUM_ROWS (fp32 partials in `part`), then
-// the chunks in order.
+// Column sums (bias gradients), one fixed-order pass.
 template <int ROLE>
-hipError_t colsum(const Dims& D, const void* X, void* out, long R, long N, long ld, float* part, hipStream_t st) {
+hipError_t colsum(const Dims& D, const void* X, void* out, long R, long N, long ld, hipStream_t st) {
   prof::Scope sc(ROLE, (double)R * N, (double)D.es * (R * N + N), st);
-  const int vec = D.dt == TP_BF16 ? 8 : 4;
-  const int chunks = (int)colsum_chunks(R);
-  const dim3 grid((unsigned)cdivl(N, 8L * vec), (unsigned)chunks);
-  const unsigned fin = (unsigned)cdivl(N, 1024);
-  if (D.dt == TP_BF16) {
-    hipLaunchKernelGGL(colsum_part_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)X, part, (int)R, (int)N, ld,
-                       COLSUM_ROWS);
-    hipLaunchKernelGGL(colsum_final_kernel<bf16_t>, dim3(fin), dim3(256), 0, st, part, (bf16_t*)out, (int)N, chunks);
-  } else {
-    hipLaunchKernelGGL(colsum_part_kernel<float>, grid, dim3(256), 0, st, (const float*)X, part, (int)R, (int)N, ld,
-                       COLSUM_ROWS);
-    hipLaunchKernelGGL(colsum_final_kernel<float>, dim3(fin), dim3(256), 0, st, part, (float*)out, (int)N, chunks);
-  }
+  if (D.dt == TP_BF16)
+    hipLaunchKernelGGL(colsum_kernel<bf16_t>, dim3((unsigned)cdivl(N, 64)), dim3(256), 0, st, (const bf16_t*)X,
+                       (bf16_t*)out, (int)R, (int)N, ld);
+  else
+    hipLaunchKernelGGL(colsum_kernel<float>, dim3((unsigned)cdivl(N, 32)), dim3(256), 0, st, (const float*)X,
+                       (float*)out, (int)R, (int)N, ld);
   return hipGetLastError();
 }
 
@@ -772,7 +759,7 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     q.C = g->dw_out; q.ldc = D.h;
     TRY((pair<EPI_LINEAR, R_O_BWD, R_O_DGRAD, R_O_WGRAD>(D, p, q, part, st)));
   }
-  TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, part, st));  // dbo (replica)
+  TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, st));  // dbo (replica)
   {  // D = rowsum(dC * C) per (sequence, head, query)
     prof::Scope sc(R_ROWDOT, 2.0 * D.T * D.hr, D.T * D.hr * (es + 4.0) + 4.0 * D.z * D.s, st);
     if (D.dt == TP_BF16) TRY(rowdot_t<bf16_t>(D, dC, C32, Dv, st));
@@ -852,7 +839,7 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     q.C = g->dw_in; q.ldc = D.q3;
     TRY((pair<EPI_LINEAR, R_QKV_BWD, R_QKV_DGRAD, R_QKV_WGRAD>(D, p, q, part, st)));
   }
-  TRY(colsum<R_DBQKV>(D, dqkv, g->db_in, D.T, D.q3, D.q3, part, st));
+  TRY(colsum<R_DBQKV>(D, dqkv, g->db_in, D.T, D.q3, D.q3, st));
   return TP_OK;
 }
 
@@ -906,7 +893,7 @@ int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void*
     q.C = g->dw_out; q.ldc = D.h;
     TRY((pair<EPI_GELU_BWD, R_FC2_BWD, R_FC2_DGRAD, R_FC2_WGRAD>(D, p, q, part, st)));
   }
-  TRY(colsum<R_DB2>(D, dy, g->db_out, D.T, D.h, D.h, part, st));  // db2 (replica)
+  TRY(colsum<R_DB2>(D, dy, g->db_out, D.T, D.h, D.h, st));  // db2 (replica)
   {  // dH_r = dU W1_r^T
     GemmArgs p = gargs(D.T, D.h, D.fr);
     p.A = dU; p.lda = D.fr;
@@ -919,7 +906,7 @@ int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void*
     q.C = g->dw_in; q.ldc = D.fr;
     TRY((pair<EPI_LINEAR, R_FC1_BWD, R_FC1_DGRAD, R_FC1_WGRAD>(D, p, q, part, st)));
   }
-  TRY(colsum<R_DB1>(D, dU, g->db_in, D.T, D.fr, D.fr, part, st));
+  TRY(colsum<R_DB1>(D, dU, g->db_in, D.T, D.fr, D.fr, st));
   return TP_OK;
 }
 
