@@ -163,10 +163,13 @@ using CfgBig = TileCfg<bf16_t, 256, 256, 2, TPL_BIG_WN>;  // linear GEMMs
 using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
 using CfgF32 = TileCfg<float, 64, 64, 2, 2>;     // fp32 configuration
 
-// Split-K for GEMMs with too few output tiles to fill 256 CUs.
+// Split-K for GEMMs with too few output tiles to fill half of the 256 CUs.
+// From 128 tiles on, one partial wave of whole tiles is faster: the busy
+// CUs run at a higher clock and share operand panels in L2, while split or
+// stream-K pieces add fp32 partial traffic and a reduction.
 int choose_splits(long M, long N, long K) {
   const long tiles = cdivl(M, CfgBig::BM) * cdivl(N, CfgBig::BN);
-  if (tiles >= 160 || K < 2048) return 1;
+  if (tiles >= 128 || K < 2048) return 1;
   long s = (256 + tiles / 2) / tiles;
   s = std::min(s, K / 1024);
   if (s < 2) return 1;
@@ -236,9 +239,16 @@ SavedLayout saved_layout(const Dims& D, int blk) {
   return L;
 }
 
+#ifndef TPL_SK_MIN_TILES
+#define TPL_SK_MIN_TILES 160
+#endif
 // Stream-K plan for a bf16 GEMM on 256x256 tiles with whole 64-deep K steps
 // (units = 0: not worth it). Whole waves of tiles run as they are; the last,
-// partial wave's K iterations are spread over all 256 CUs. Chosen when the
+// partial wave's K iterations are spread over all 256 CUs. Without a whole
+// wave in front, the pieces start at staggered K offsets, so no two CUs of
+// an XCD share an operand slice in L2 and every piece's panels come from
+// beyond L2 (measured: 10x the operand bytes for a 144-tile GEMM); below
+// TPL_SK_MIN_TILES tiles a partial wave of whole tiles wins instead. Chosen when the
 // modelled time beats the plain (or split-K) launch; the model counts one
 // tile-iteration as ~1.95 us and charges the fp32 fragments' write + read at
 // ~5 TB/s plus a launch gap for the fix-up.
@@ -249,6 +259,7 @@ SkPlan sk_plan(long M, long N, long K) {
   const long I = K / CfgBig::BK;
   const long W = tiles / 256, R = tiles % 256;
   if (R == 0 || I < 8) return s;
+  if (W == 0 && tiles < TPL_SK_MIN_TILES) return s;  // too few tiles: a partial wave of whole tiles
   const double t_it = 1.95e-6, frag = 4.0 * CfgBig::BM * CfgBig::BN;
   double plain = (double)cdivl(tiles, 256) * I * t_it;
   const int sp = choose_splits(M, N, K);

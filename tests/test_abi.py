@@ -122,10 +122,13 @@ def test_reduce_and_gemm_validation_on_host():
     assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, a, _fake(0x100008), none, a, None) == tp.TP_EALIGN
     assert L.tp_gemm(tp.TP_BF16, 20, 16, 16, 1.0, a, 16, 1, a, 16, 1, None, a, 16, None, 0, None) == tp.TP_EUNSUPPORTED
     assert L.tp_gemm(tp.TP_BF16, 16, 16, 32, 1.0, a, 16, 1, a, 32, 1, None, a, 16, None, 0, None) == tp.TP_EINVAL
-    # stream-K over a partial last wave needs fp32 fragment slots: workspace checked before any launch
-    M, N, K = 2048, 6144, 12288
+    # stream-K over the partial wave behind a whole one needs fp32 fragment slots (384 tiles: 128 tiles in
+    # 2 pieces each): workspace checked before any launch
+    M, N, K = 2048, 12288, 6144
     need = tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K)
-    assert need >= 192 * 2 * 256 * 256 * 4
+    assert need >= 128 * 2 * 256 * 256 * 4
+    # fewer than 160 tiles (and at least 128) run as one partial wave of whole tiles and need none
+    assert tp.tp_gemm_workspace_bytes(tp.TP_BF16, 2048, 4608, 12288) == 0
     assert L.tp_gemm(tp.TP_BF16, M, N, K, 1.0, a, K, 1, a, N, 0, None, a, N, a, need - 256, None) == tp.TP_EWORKSPACE
     assert L.tp_gemm(tp.TP_BF16, M, N, K, 1.0, a, K, 1, a, N, 0, None, a, N, none, need, None) == tp.TP_ENULL
     # small problems need none; fp32 never does

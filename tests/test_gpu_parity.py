@@ -56,15 +56,15 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
 # without whole waves before it, ragged M and N, 3 and 6 fragments per tile)
 # and split-K. Rows sampled (first, last, scattered), every column, fp64
 # reference from the same bf16 operands; a second call must match bitwise.
-@pytest.mark.parametrize("M,N,K,ak,bk", [
-    (2064, 4624, 12288, 1, 0),   # 171 tiles < one wave: all stream-K (c = 129 of 192 iterations)
-    (2064, 4624, 12288, 1, 1),
-    (2064, 8208, 6144, 0, 0),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
-    (2064, 8208, 6144, 0, 1),
-    (1040, 2832, 4096, 1, 0),    # 60 tiles: split-K
+@pytest.mark.parametrize("M,N,K,ak,bk,plan", [
+    (2064, 4624, 12288, 1, 0, "sk"),   # 171 tiles < one wave: all stream-K (c = 129 of 192 iterations)
+    (2064, 4112, 12288, 1, 1, "dp"),   # 153 tiles: one partial wave of whole tiles
+    (2064, 8208, 6144, 0, 0, "sk"),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
+    (2064, 8208, 6144, 0, 1, "sk"),
+    (1040, 2832, 4096, 1, 0, "split"),  # 60 tiles: split-K
 ])
-def test_gemm_launch_plans_full_size(M, N, K, ak, bk):
-    print(f"gemm plan {M}x{N}x{K} ak={ak} bk={bk}", flush=True)
+def test_gemm_launch_plans_full_size(M, N, K, ak, bk, plan):
+    print(f"gemm plan {M}x{N}x{K} ak={ak} bk={bk} ({plan})", flush=True)
     rng = np.random.default_rng(M + N + K + 2 * ak + bk)
     A = I.round_to_bf16(rng.standard_normal((M, K), dtype=np.float32))
     B = I.round_to_bf16(rng.standard_normal((K, N), dtype=np.float32))
@@ -73,7 +73,8 @@ def test_gemm_launch_plans_full_size(M, N, K, ak, bk):
     Ad = torch.from_numpy(A if ak else np.ascontiguousarray(A.T)).to("cuda", bf)
     Bd = torch.from_numpy(np.ascontiguousarray(B.T) if bk else B).to("cuda", bf)
     bd = torch.from_numpy(bias).to("cuda", bf)
-    assert tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K) > 0
+    # stream-K and split-K keep fp32 partials in the workspace; whole tiles need none
+    assert (tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K) > 0) == (plan != "dp")
     outs = []
     for _ in range(2):
         C = torch.full((M, N), float("nan"), device="cuda", dtype=bf)
