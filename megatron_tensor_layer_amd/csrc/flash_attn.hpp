@@ -21,13 +21,19 @@
 // three MFMA passes keep about 16 mantissa bits of the logits, which the
 // peaked softmax rows of wide layers need.
 //
-// Kernels (4 waves of 64 lanes, one workgroup per CU):
+// Kernels (4 waves of 64 lanes):
 //   fa_fwd_kernel    : 128 queries (32 per wave); keys in tiles of 64 staged
 //                      in LDS (Kh, Kl, V; double buffered); writes C (bf16 and
-//                      fp32) and the log2-domain log-sum-exp.
+//                      fp32) and the log2-domain log-sum-exp. fa_fwd2_kernel is
+//                      the same with single-buffered tiles: within 256
+//                      registers per lane and 48 KB of LDS (d <= 128), two
+//                      workgroups share a CU and one computes while the other
+//                      waits for its tile (the scores' VALU work and the MFMAs
+//                      of one wave cannot overlap much on their own).
 //   fa_bwd_dkv_kernel: 128 keys (32 per wave); queries in tiles of 64 (Qh,
 //                      Ql, dC + LSE and D); accumulates dK, dV.
-//   fa_bwd_dq_kernel : 128 queries; keys in tiles of 64; dQ.
+//   fa_bwd_dq_kernel : 128 queries; keys in tiles of 64; dQ (fa_bwd_dq2_kernel:
+//                      single-buffered, two workgroups per CU).
 // dQ has its own kernel (recomputing P and dP) so that every gradient is a
 // fixed-order sum: no atomics, bitwise reproducible.
 //
@@ -379,11 +385,13 @@ __device__ __forceinline__ void rows_store(bf16_t* dst, float* dst32, const f32x
 // forward: 1-D grid of z * items workgroups; one item = one chunk of key
 // tiles of a block of 128 queries
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) fa_fwd_kernel(const FaArgs a) {
+// NBUF = 2: one workgroup per CU, the next key tile loads while this one is
+// computed. NBUF = 1: single-buffered tiles (48 KB of LDS at d = 128) so that
+// two workgroups share a CU and each computes while the other waits.
+template <int D, int NBUF>
+__device__ __forceinline__ void fa_fwd_body(const FaArgs& a, uint4* lds) {
   constexpr int DP = (D + 63) / 64 * 64, KS = D / 16, NB = D / 32;
   using TL = fa::Tile<DP>;
-  __shared__ __attribute__((aligned(1024))) uint4 lds[2 * 3 * TL::U4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int z, idx;
@@ -433,9 +441,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       ek.issue(Vv + r0 * ld, L + 2 * TL::U4, wave);
     }
   };
-  auto step = [&](auto bufc, int t) {
+  auto compute = [&](auto bufc, int t) {
     constexpr int BUF = decltype(bufc)::value;
-    if (t + 1 < it.t1) issue(t + 1, BUF ^ 1);
     const uint4* Lk = lds + BUF * 3 * TL::U4;
     if (t < wt) {
       f32x16_t sacc[2];
@@ -481,15 +488,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       l += rs + fa::xlane32(rs);
       fa::tr_products<NB>(Lk + 2 * TL::U4, lo, sacc, o);
     }
+  };
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (t + 1 < it.t1) issue(t + 1, BUF ^ 1);
+    compute(bufc, t);
     wait_loads();
     __syncthreads();
   };
-  issue(it.t0, 0);
-  wait_loads();
-  __syncthreads();
-  for (int t = it.t0; t < it.t1; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < it.t1) step(std::integral_constant<int, 1>{}, t + 1);
+  if constexpr (NBUF == 2) {
+    issue(it.t0, 0);
+    wait_loads();
+    __syncthreads();
+    for (int t = it.t0; t < it.t1; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < it.t1) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  } else {
+    for (int t = it.t0; t < it.t1; ++t) {
+      issue(t, 0);
+      wait_loads();
+      __syncthreads();
+      compute(std::integral_constant<int, 0>{}, t);
+      __syncthreads();
+    }
   }
 
   if (it.nch > 1) {  // partial: unnormalised C, running maximum and sum
@@ -503,6 +525,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     fa::rows_store<NB>(a.ctx + trow * a.hr + head * a.d, a.ctx32 + trow * a.hr + head * a.d, o, 1.0f / l, g);
     if (g == 0) a.lse[(long)z * a.s + qrow] = m + __log2f(l);
   }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) fa_fwd_kernel(const FaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint4 lds[2 * 3 * fa::Tile<(D + 63) / 64 * 64>::U4];
+  fa_fwd_body<D, 2>(a, lds);
+}
+template <int D>
+__global__ void __launch_bounds__(256, 2) fa_fwd2_kernel(const FaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint4 lds[3 * fa::Tile<(D + 63) / 64 * 64>::U4];
+  fa_fwd_body<D, 1>(a, lds);
 }
 
 // Forward combine: grid (blocks * D / 8, z), one float4 of a block's
@@ -683,12 +716,10 @@ fa_bwd_dkv_kernel(const FaArgs a) {
 // ---------------------------------------------------------------------------
 // backward, dQ: items as in the forward pass
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-fa_bwd_dq_kernel(const FaArgs a) {
+template <int D, int NBUF>
+__device__ __forceinline__ void fa_dq_body(const FaArgs& a, uint4* lds) {
   constexpr int DP = (D + 63) / 64 * 64, KS = D / 16, NB = D / 32;
   using TL = fa::Tile<DP>;
-  __shared__ __attribute__((aligned(1024))) uint4 lds[2 * 3 * TL::U4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int z, idx;
@@ -744,9 +775,8 @@ fa_bwd_dq_kernel(const FaArgs a) {
       ek.issue(Vv + r0 * ld, L + 2 * TL::U4, wave);
     }
   };
-  auto step = [&](auto bufc, int t) {
+  auto compute = [&](auto bufc, int t) {
     constexpr int BUF = decltype(bufc)::value;
-    if (t + 1 < it.t1) issue(t + 1, BUF ^ 1);
     const uint4* Lk = lds + BUF * 3 * TL::U4;
     if (t < wt) {
       f32x16_t sacc[2], dp[2];
@@ -770,15 +800,30 @@ fa_bwd_dq_kernel(const FaArgs a) {
         }
       fa::tr_products<NB>(Lk, lo, dp, dq);  // dQ += dS Kh
     }
+  };
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (t + 1 < it.t1) issue(t + 1, BUF ^ 1);
+    compute(bufc, t);
     wait_loads();
     __syncthreads();
   };
-  issue(it.t0, 0);
-  wait_loads();
-  __syncthreads();
-  for (int t = it.t0; t < it.t1; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < it.t1) step(std::integral_constant<int, 1>{}, t + 1);
+  if constexpr (NBUF == 2) {
+    issue(it.t0, 0);
+    wait_loads();
+    __syncthreads();
+    for (int t = it.t0; t < it.t1; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < it.t1) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  } else {
+    for (int t = it.t0; t < it.t1; ++t) {
+      issue(t, 0);
+      wait_loads();
+      __syncthreads();
+      compute(std::integral_constant<int, 0>{}, t);
+      __syncthreads();
+    }
   }
 
   if (it.nch > 1) {
@@ -787,6 +832,18 @@ fa_bwd_dq_kernel(const FaArgs a) {
     const long trow = (long)qrow * a.b + beta;
     fa::rows_store<NB>(a.dqkv + trow * a.q3 + head * a.d, nullptr, dq, 1.0f, g);
   }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dq_kernel(const FaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint4 lds[2 * 3 * fa::Tile<(D + 63) / 64 * 64>::U4];
+  fa_dq_body<D, 2>(a, lds);
+}
+template <int D>
+__global__ void __launch_bounds__(256, 2) fa_bwd_dq2_kernel(const FaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint4 lds[3 * fa::Tile<(D + 63) / 64 * 64>::U4];
+  fa_dq_body<D, 1>(a, lds);
 }
 
 // Backward combine: grid (blocks * D / 8, z), one float4 per thread per

@@ -616,10 +616,13 @@ FaArgs fa_args(const Dims& D) {
       default: return hipErrorInvalidValue;                                                   \
     }                                                                                         \
   } while (0)
-#define TPL_FA_FWD(DD) fa_fwd_kernel<DD>
+// Head widths up to 128 run the forward and dQ kernels with single-buffered
+// tiles, two workgroups per CU (they fit 256 registers per lane); d = 160 and
+// the dK/dV kernel keep one double-buffered workgroup per CU.
+#define TPL_FA_FWD(DD) (DD <= 128 ? fa_fwd2_kernel<DD> : fa_fwd_kernel<DD>)
 #define TPL_FA_FWD_COMBINE(DD) fa_fwd_combine_kernel<DD>
 #define TPL_FA_DKV(DD) fa_bwd_dkv_kernel<DD>
-#define TPL_FA_DQ(DD) fa_bwd_dq_kernel<DD>
+#define TPL_FA_DQ(DD) (DD <= 128 ? fa_bwd_dq2_kernel<DD> : fa_bwd_dq_kernel<DD>)
 #define TPL_FA_KV_COMBINE(DD) (fa_bwd_combine_kernel<DD, true>)
 #define TPL_FA_Q_COMBINE(DD) (fa_bwd_combine_kernel<DD, false>)
 
