@@ -109,6 +109,9 @@ SMALL = {
     # bf16, d = 128, sequence long enough (18 key tiles of 64) that the fused
     # attention cuts the longer causal ranges into chunks and merges them
     "bf16_chunked": I.make_config("bf16_chunked", h=256, a=2, s=1152, b=1, t=2, dtype="bf16"),
+    # bf16, d = 64, a sequence shorter than one 64-key tile (s = 16): the fused
+    # attention's partial tiles, clamped rows and LSE chunks at their smallest
+    "bf16_short": I.make_config("bf16_short", h=128, a=2, s=16, b=3, t=2, dtype="bf16"),
     # bf16 with a head width the fused attention kernels are not built for
     # (d = 48): attention through the materialised s x s GEMM path
     "bf16_d48": I.make_config("bf16_d48", h=192, a=4, s=96, b=2, t=2, dtype="bf16"),
