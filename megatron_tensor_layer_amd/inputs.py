@@ -148,6 +148,25 @@ def params_rank(cfg: LayerConfig, r: int) -> dict:
     return {n: param_part(cfg, n, r) for n in PARAM_NAMES}
 
 
+# LayerNorm weights (g1, g2) ~ 1 + N(0, 0.1^2) and biases (be1, be2) ~
+# N(0, 0.02^2), each [h] and replicated on every rank.  The pages give no
+# initialisation; the spread of the weights around 1 makes a transposed or
+# misindexed weight visible in the tests.
+LN_WEIGHT_STD = 0.1
+LN_NAMES = ("g1", "be1", "g2", "be2")
+
+
+def ln_param(cfg: LayerConfig, name: str) -> np.ndarray:
+    if name in ("g1", "g2"):
+        x = draw(cfg.name, name, (cfg.h,), LN_WEIGHT_STD, "fp32") + np.float32(1.0)
+        return round_to_bf16(x) if cfg.dtype == "bf16" else x.astype(np.float32)
+    return draw(cfg.name, name, (cfg.h,), WEIGHT_STD, cfg.dtype)
+
+
+def ln_params(cfg: LayerConfig) -> dict:
+    return {n: ln_param(cfg, n) for n in LN_NAMES}
+
+
 def activation(cfg: LayerConfig, name: str = "X", tokens: int | None = None) -> np.ndarray:
     """[tokens, h] token-major activation or gradient, N(0, 1)."""
     T = cfg.tokens if tokens is None else tokens

@@ -7,8 +7,9 @@ the HIP library and never imports it; the product path must never call it.
 
 What it computes
 ----------------
-The unsharded layer is the attention block followed by the MLP block, causal,
-dropout-free, with a residual add after each block and no LayerNorm:
+The hot-path form of the unsharded layer is the attention block followed by
+the MLP block, causal, dropout-free, with a residual add after each block and
+no LayerNorm:
 
     Q = X Wq + bq,  K = X Wk + bk,  V = X Wv + bv
     per sequence beta and head j:  S = Q_bj K_bj^T / sqrt(d),
@@ -45,6 +46,28 @@ QKV shard of rank r is the contiguous column range c_r of each of Wq, Wk, Wv;
 replicated terms (the output bias and the residual) are added once, after
 the all-reduce of the partials, as the fused bias+dropout+add of the
 paper-graph page's "Computation Optimizations" (here without dropout).
+
+A second form of the layer adds the two LayerNorms of the GPT layer in
+front of the blocks (pre-norm) and runs it with sequence parallelism: each
+rank applies the LayerNorms, the biases after the row-parallel products and
+the residual adds to its own contiguous slice of the sequence, the all-reduce
+becomes a reduce-scatter along the sequence before that region and an
+all-gather after it:
+
+    A = LN1(X),  H = X + attn(A) Wo + bo,  B = LN2(H),  Y = H + MLP(B) + b2
+    LN(x) = (x - mean(x)) / sqrt(var(x) + eps) * gamma + beta   per token,
+        mean and (biased) variance over the token's h features, eps = 1e-5
+
+Sources: "parallelism" blog post, "Sequence parallelism: the parts TP leaves
+behind" (LayerNorm, dropout and the residual add split by tokens; the
+all-reduce as reduce-scatter plus all-gather; LayerNorm on the rank's tokens,
+then all-gather, the sharded products, reduce-scatter, then the residual),
+and the same page's hybrid-parallelism walk-through (the gradients of the
+replicated LayerNorm weights are partial per rank and are summed over the
+tensor-parallel group); "Distributed training" (ML interview book), section
+2.2 (two LayerNorms per layer, each storing its input; sequence parallelism
+shards them along s).  The pages do not write LayerNorm out: the textbook
+definition above is used, with biased variance and eps = 1e-5 (readings).
 
 Parity pins live in tests/test_oracle_pins.py: the blog's worked MLP values,
 closed forms of GELU and the softmax, brute-force loops on tiny inputs,
@@ -339,3 +362,161 @@ def model_flops_per_rank(h, s, b, t):
     """72 b s h^2 (1 + s / 6h) / t: forward (24 b s h^2 (1 + s/6h)) plus a
     backward of twice that, for one layer, shared evenly over t ranks."""
     return 72.0 * b * s * h * h * (1.0 + s / (6.0 * h)) / t
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm and the pre-norm layer with sequence parallelism
+# ---------------------------------------------------------------------------
+
+LN_EPS = 1e-5
+LN_NAMES = ("g1", "be1", "g2", "be2")  # LN1 weight / bias, LN2 weight / bias
+
+
+def layer_norm(x, gamma, beta, eps=LN_EPS):
+    """Per token (row): normalise over the h features with the mean and the
+    biased variance, then scale by gamma and shift by beta.  Returns the
+    output and the cache for the backward pass (x_hat and 1/sqrt(var+eps))."""
+    x = np.asarray(x, dtype=F64)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = (x - mean) * rstd
+    return xhat * gamma + beta, dict(xhat=xhat, rstd=rstd, mean=mean)
+
+
+def layer_norm_backward(cache, gamma, dy):
+    """Chain rule through y = gamma * x_hat + beta, x_hat = (x - mean) rstd:
+    with g = dy * gamma, dx = rstd (g - mean(g) - x_hat mean(g x_hat));
+    dgamma = sum over tokens of dy x_hat, dbeta = sum over tokens of dy."""
+    dy = np.asarray(dy, dtype=F64)
+    xhat, rstd = cache["xhat"], cache["rstd"]
+    g = dy * gamma
+    dx = rstd * (g - g.mean(axis=-1, keepdims=True) - xhat * (g * xhat).mean(axis=-1, keepdims=True))
+    return dx, (dy * xhat).sum(axis=0), dy.sum(axis=0)
+
+
+def attention_branch_forward(A, p, s, b, n_heads):
+    """C Wo for the attention block fed with A (no bias, no residual)."""
+    A = np.asarray(A, dtype=F64)
+    Q = A @ p["Wq"] + p["bq"]
+    K = A @ p["Wk"] + p["bk"]
+    V = A @ p["Wv"] + p["bv"]
+    C, P = attention_core_forward(Q, K, V, s, b, n_heads)
+    return C @ p["Wo"], dict(X=A, Q=Q, K=K, V=V, P=P, C=C)
+
+
+def prenorm_layer_forward(X, p, ln, s, b, n_heads):
+    """The unsharded pre-norm layer: A = LN1(X), H = X + attn(A) Wo + bo,
+    B = LN2(H), Y = H + MLP(B) + b2 (biases of all four linears, exact GELU)."""
+    X = np.asarray(X, dtype=F64)
+    A, c1 = layer_norm(X, ln["g1"], ln["be1"])
+    att, ca = attention_branch_forward(A, p, s, b, n_heads)
+    H = X + att + p["bo"]
+    B, c2 = layer_norm(H, ln["g2"], ln["be2"])
+    mo, cm = mlp_branch_forward(B, p["W1"], p["b1"], p["W2"], p["b2"])
+    Y = H + mo
+    return Y, dict(X=X, A=A, H=H, B=B, ln1=c1, ln2=c2, attn=ca, mlp=cm)
+
+
+def prenorm_layer_backward(cache, p, ln, dY, s, b, n_heads):
+    """Gradients of the pre-norm layer for the upstream gradient dY: every
+    weight and bias, the four LayerNorm parameters, dH and dX."""
+    dY = np.asarray(dY, dtype=F64)
+    g = mlp_branch_backward(cache["mlp"], p["W1"], p["W2"], dY)
+    dB = g.pop("dH")
+    dH_ln, g["dg2"], g["dbe2"] = layer_norm_backward(cache["ln2"], ln["g2"], dB)
+    dH = dY + dH_ln                       # residual path + through LN2
+    ga = attention_rank_backward(cache["attn"], p, dH, s, b, n_heads)
+    dA = ga.pop("dX")
+    ga.pop("dC")
+    g.update(ga)
+    dX_ln, g["dg1"], g["dbe1"] = layer_norm_backward(cache["ln1"], ln["g1"], dA)
+    g["dX"] = dH + dX_ln                  # residual path + through LN1
+    g["dH"] = dH
+    return g
+
+
+def seq_range(tokens, r, t):
+    """Rank r's contiguous slice of the token rows.  Rows are token-major
+    (row = sigma * b + beta), so the slice is the positions
+    [r s / t, (r + 1) s / t) of every sequence."""
+    return col_range(tokens, r, t)
+
+
+def all_gather_rows(slices):
+    """Stand-in for the all-gather along the sequence: rank slices in order."""
+    return np.concatenate([np.asarray(x, dtype=F64) for x in slices], axis=0)
+
+
+def reduce_scatter_rows(partials, r, t):
+    """Stand-in for the reduce-scatter along the sequence: rank r's slice of
+    the element-wise sum over ranks."""
+    tot = all_reduce_sum(partials)
+    return tot[seq_range(tot.shape[0], r, t)]
+
+
+def sp_layer_forward(X, p, ln, s, b, n_heads, t):
+    """The pre-norm layer as t sequence- and tensor-parallel ranks compute it.
+
+    Per rank r, with x_r its token slice of X:
+      a_r = LN1(x_r);  A = all-gather(a_r);  part_r = attn_r(A) Wo_r
+      h_r = reduce-scatter(part)_r + bo + x_r;  b_r = LN2(h_r);  B = all-gather(b_r)
+      part_r = MLP_r(B);  y_r = reduce-scatter(part)_r + b2 + h_r
+    Returns the rank outputs y_r (their concatenation is Y) and per-rank caches."""
+    X = np.asarray(X, dtype=F64)
+    T = X.shape[0]
+    ar = n_heads // t
+    ranks = [dict(pr=shard_params(p, r, t), x=X[seq_range(T, r, t)]) for r in range(t)]
+    for rk in ranks:
+        rk["a"], rk["ln1"] = layer_norm(rk["x"], ln["g1"], ln["be1"])
+    A = all_gather_rows([rk["a"] for rk in ranks])
+    parts = []
+    for rk in ranks:
+        part, rk["attn"] = attention_rank_forward(A, rk["pr"], s, b, ar)
+        parts.append(part)
+    for r, rk in enumerate(ranks):
+        rk["h"] = reduce_scatter_rows(parts, r, t) + p["bo"] + rk["x"]
+        rk["b"], rk["ln2"] = layer_norm(rk["h"], ln["g2"], ln["be2"])
+    B = all_gather_rows([rk["b"] for rk in ranks])
+    parts = []
+    for rk in ranks:
+        part, rk["mlp"] = mlp_rank_forward(B, rk["pr"])
+        parts.append(part)
+    ys = [reduce_scatter_rows(parts, r, t) + p["b2"] + rk["h"] for r, rk in enumerate(ranks)]
+    return ys, ranks
+
+
+def sp_layer_backward(ranks, ln, dys, s, b, n_heads, t):
+    """Backward of sp_layer_forward for the rank slices dy_r of dY.
+
+    Per rank r:
+      dY = all-gather(dy_r);  MLP_r backward -> part_r (and the W1/b1/W2 shards, db2)
+      dh_r = LN2 backward of reduce-scatter(part)_r + dy_r   (dg2_r, dbe2_r partial)
+      dH = all-gather(dh_r);  attention_r backward -> part_r (QKV/Wo shards, dbo)
+      dx_r = LN1 backward of reduce-scatter(part)_r + dh_r   (dg1_r, dbe1_r partial)
+    The LayerNorm parameter gradients of a rank cover its own tokens only:
+    their sum over ranks is the full gradient.  Returns per-rank dicts."""
+    T = sum(np.asarray(d).shape[0] for d in dys)
+    ar = n_heads // t
+    dY = all_gather_rows(dys)
+    out = [dict() for _ in range(t)]
+    parts = []
+    for r, rk in enumerate(ranks):
+        g = mlp_rank_backward(rk["mlp"], rk["pr"], dY)
+        parts.append(g.pop("dH"))
+        out[r].update(g)
+    for r, rk in enumerate(ranks):
+        dln, out[r]["dg2"], out[r]["dbe2"] = layer_norm_backward(rk["ln2"], ln["g2"], reduce_scatter_rows(parts, r, t))
+        out[r]["dh"] = dln + np.asarray(dys[r], dtype=F64)
+    dH = all_gather_rows([o["dh"] for o in out])
+    parts = []
+    for r, rk in enumerate(ranks):
+        g = attention_rank_backward(rk["attn"], rk["pr"], dH, s, b, ar)
+        parts.append(g.pop("dX"))
+        g.pop("dC")
+        out[r].update(g)
+    for r, rk in enumerate(ranks):
+        dln, out[r]["dg1"], out[r]["dbe1"] = layer_norm_backward(rk["ln1"], ln["g1"], reduce_scatter_rows(parts, r, t))
+        out[r]["dx"] = dln + out[r]["dh"]
+    assert dY.shape[0] == T
+    return out

@@ -42,3 +42,14 @@ def test_draws_are_deterministic_and_part_addressable():
 def test_prefix_of_a_draw_is_the_shorter_draw():
     c = I.make_config("tiny", h=32, a=4, s=8, b=2, t=4, dtype="fp32")
     np.testing.assert_array_equal(I.activation(c, "X")[:6], I.activation(c, "X", tokens=6))
+
+
+def test_layernorm_params_are_rounded_and_spread_around_one():
+    c = I.make_config("ln", h=4096, a=32, s=16, b=1, t=8, dtype="bf16")
+    ln = I.ln_params(c)
+    for n in I.LN_NAMES:
+        assert ln[n].shape == (4096,)
+        np.testing.assert_array_equal(ln[n], I.round_to_bf16(ln[n]))
+    assert abs(float(np.mean(ln["g1"])) - 1.0) < 0.01 and abs(float(np.std(ln["g1"])) - 0.1) < 0.01
+    assert abs(float(np.std(ln["be2"])) - 0.02) < 0.003
+    assert not np.array_equal(ln["g1"], ln["g2"])

@@ -356,3 +356,160 @@ def test_flops_formula_equals_gemm_count(name):
     # scores and context, full s^2 per (sequence, head) as Eq. 3 counts them
     fwd += 2 * (2 * b * (c.a // t) * s * s * c.d)
     assert 3 * fwd == pytest.approx(O.model_flops_per_rank(h, s, b, t), rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm and the pre-norm layer with sequence parallelism
+# ---------------------------------------------------------------------------
+
+def _rand_ln(rng, h):
+    return {"g1": 1.0 + 0.3 * rng.standard_normal(h), "be1": 0.3 * rng.standard_normal(h),
+            "g2": 1.0 + 0.3 * rng.standard_normal(h), "be2": 0.3 * rng.standard_normal(h)}
+
+
+def test_layer_norm_closed_forms():
+    rng = np.random.default_rng(50)
+    x = rng.standard_normal((5, 12)) * 3.0 + 7.0
+    one, zero = np.ones(12), np.zeros(12)
+    y, _ = O.layer_norm(x, one, zero)
+    var = x.var(axis=1)                      # biased variance, numpy's definition
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), var / (var + O.LN_EPS), rtol=1e-13)
+    # two features: the output is -c, +c with c = |a - b| / 2 / sqrt(((a - b) / 2)^2 + eps)
+    for a, b in ((1.0, 3.0), (-2.0, 0.5), (4.0, 4.0)):
+        half = (b - a) / 2.0
+        c = half / math.sqrt(half * half + O.LN_EPS)
+        np.testing.assert_allclose(O.layer_norm(np.array([[a, b]]), np.ones(2), np.zeros(2))[0], [[-c, c]],
+                                   atol=1e-15)
+    # without eps, LN is invariant to a positive scale and a shift of the token
+    y0, _ = O.layer_norm(x, one, zero, eps=0.0)
+    y1, _ = O.layer_norm(2.5 * x - 4.0, one, zero, eps=0.0)
+    np.testing.assert_allclose(y0, y1, atol=1e-12)
+    # gamma and beta act per feature after the normalisation
+    g, be = rng.standard_normal(12), rng.standard_normal(12)
+    np.testing.assert_allclose(O.layer_norm(x, g, be)[0], y * g + be, atol=1e-13)
+
+
+def test_layer_norm_matches_torch_in_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((7, 24)) * 2.0 + 0.5
+    g, be, dy = rng.standard_normal(24), rng.standard_normal(24), rng.standard_normal((7, 24))
+    y, cache = O.layer_norm(x, g, be)
+    dx, dg, dbe = O.layer_norm_backward(cache, g, dy)
+    tx, tg, tb = (torch.tensor(v, dtype=torch.float64, requires_grad=True) for v in (x, g, be))
+    ty = torch.nn.functional.layer_norm(tx, (24,), tg, tb, eps=O.LN_EPS)
+    ty.backward(torch.tensor(dy, dtype=torch.float64))
+    np.testing.assert_allclose(y, ty.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dx, tx.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dg, tg.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dbe, tb.grad.numpy(), atol=1e-12)
+
+
+def test_layer_norm_backward_finite_differences():
+    rng = np.random.default_rng(52)
+    x, g, be, dy = (rng.standard_normal(sh) for sh in ((4, 6), (6,), (6,), (4, 6)))
+    _, cache = O.layer_norm(x, g, be)
+    dx, dg, dbe = O.layer_norm_backward(cache, g, dy)
+    loss = lambda xx, gg, bb: float(np.sum(O.layer_norm(xx, gg, bb)[0] * dy))  # noqa: E731
+    eps = 1e-6
+    for arr, grad, which in ((x, dx, 0), (g, dg, 1), (be, dbe, 2)):
+        for fi in range(arr.size):
+            idx = np.unravel_index(fi, arr.shape)
+            args_p = [x.copy(), g.copy(), be.copy()]
+            args_m = [x.copy(), g.copy(), be.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+    # the gradient with respect to x is orthogonal to the shift direction
+    np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-12)
+
+
+def test_prenorm_layer_structure():
+    """With gamma = 1 and beta = 0 the blocks of the pre-norm layer are the
+    hot-path blocks fed with normalised activations, while the residual
+    stream carries X and H themselves, not their normalised forms."""
+    rng = np.random.default_rng(53)
+    h, a, s, b = 16, 2, 4, 2
+    p = _rand_params(rng, h, 4 * h)
+    ln = {"g1": np.ones(h), "be1": np.zeros(h), "g2": np.ones(h), "be2": np.zeros(h)}
+    X = rng.standard_normal((s * b, h))
+    Y, c = O.prenorm_layer_forward(X, p, ln, s, b, a)
+    A = O.layer_norm(X, np.ones(h), np.zeros(h))[0]
+    att, _ = O.attention_branch_forward(A, p, s, b, a)
+    np.testing.assert_allclose(c["H"], X + att + p["bo"], atol=1e-13)
+    H_plain, _ = O.attention_block_forward(A, p, s, b, a)           # A + C Wo + bo
+    np.testing.assert_allclose(c["H"] - X, H_plain - A, atol=1e-13)
+    B = O.layer_norm(c["H"], np.ones(h), np.zeros(h))[0]
+    np.testing.assert_allclose(Y - c["H"], O.mlp_block_forward(B, p)[0] - B, atol=1e-13)
+
+
+@pytest.mark.parametrize("shape", [(8, 2, 4, 2), (12, 3, 3, 2)])
+def test_prenorm_gradients_finite_differences(shape):
+    h, a, s, b = shape
+    rng = np.random.default_rng(60 + h)
+    p = _rand_params(rng, h, 4 * h, std=0.4)
+    ln = _rand_ln(rng, h)
+    X = rng.standard_normal((s * b, h))
+    dY = rng.standard_normal((s * b, h))
+    _, cache = O.prenorm_layer_forward(X, p, ln, s, b, a)
+    g = O.prenorm_layer_backward(cache, p, ln, dY, s, b, a)
+
+    def loss(pp, ll, XX):
+        return float(np.sum(O.prenorm_layer_forward(XX, pp, ll, s, b, a)[0] * dY))
+
+    eps = 1e-5
+    for name, arr in dict(p, X=X, **ln).items():
+        grad = g["d" + name]
+        for fi in rng.choice(arr.size, size=min(arr.size, 5), replace=False):
+            idx = np.unravel_index(fi, arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            if name == "X":
+                fd = (loss(p, ln, plus) - loss(p, ln, minus)) / (2 * eps)
+            elif name in ln:
+                fd = (loss(p, dict(ln, **{name: plus}), X) - loss(p, dict(ln, **{name: minus}), X)) / (2 * eps)
+            else:
+                fd = (loss(dict(p, **{name: plus}), ln, X) - loss(dict(p, **{name: minus}), ln, X)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_sequence_parallel_equals_unsharded(t):
+    rng = np.random.default_rng(70 + t)
+    h, a, s, b = 32, 8, 8, 2
+    p = _rand_params(rng, h, 4 * h, std=0.2)
+    ln = _rand_ln(rng, h)
+    X = rng.standard_normal((s * b, h))
+    dY = rng.standard_normal((s * b, h))
+    Y, cache = O.prenorm_layer_forward(X, p, ln, s, b, a)
+    g = O.prenorm_layer_backward(cache, p, ln, dY, s, b, a)
+    T = s * b
+    ys, ranks = O.sp_layer_forward(X, p, ln, s, b, a, t)
+    for r in range(t):  # each rank holds exactly its tokens of H and Y
+        np.testing.assert_allclose(ranks[r]["h"], cache["H"][O.seq_range(T, r, t)], atol=1e-12)
+    np.testing.assert_allclose(O.all_gather_rows(ys), Y, atol=1e-12)
+    gs = O.sp_layer_backward(ranks, ln, [dY[O.seq_range(T, r, t)] for r in range(t)], s, b, a, t)
+    np.testing.assert_allclose(O.all_gather_rows([x["dx"] for x in gs]), g["dX"], atol=1e-12)
+    np.testing.assert_allclose(O.all_gather_rows([x["dh"] for x in gs]), g["dH"], atol=1e-12)
+    # LayerNorm parameters: rank gradients are partial sums over own tokens
+    for name in ("dg1", "dbe1", "dg2", "dbe2"):
+        np.testing.assert_allclose(O.all_reduce_sum([x[name] for x in gs]), g[name], atol=1e-12)
+    # tensor-parallel shards and replicas as in the hot-path layer
+    for name, axis in (("dW1", 1), ("db1", 0), ("dW2", 0), ("dWq", 1), ("dWk", 1), ("dWv", 1),
+                       ("dbq", 0), ("dbk", 0), ("dbv", 0), ("dWo", 0)):
+        np.testing.assert_allclose(np.concatenate([x[name] for x in gs], axis=axis), g[name], atol=1e-12)
+    for x in gs:
+        np.testing.assert_allclose(x["db2"], g["db2"], atol=1e-12)
+        np.testing.assert_allclose(x["dbo"], g["dbo"], atol=1e-12)
+
+
+def test_sequence_slices_are_positions_of_every_sequence():
+    s, b, t = 8, 3, 4
+    rows = np.arange(s * b)
+    for r in range(t):
+        sl = rows[O.seq_range(s * b, r, t)]
+        np.testing.assert_array_equal(np.unique(sl // b), np.arange(r * s // t, (r + 1) * s // t))
+        np.testing.assert_array_equal(np.bincount(sl % b), np.full(b, s // t))
