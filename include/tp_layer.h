@@ -87,9 +87,11 @@ typedef struct {
 int tp_check_args(int h, int a, int s, int b, int t, int rank, int dtype, int block);
 
 /* Bytes of activations that tp_layer_fwd(block, rank) saves for
- * tp_layer_bwd(block, rank): ATTN keeps QKV_r [T,3h/t], the causal softmax
- * P_r [b*a_r, s, s] and the context C_r [T,h/t]; MLP keeps U_r and Z_r
- * [T,4h/t]. 0 on invalid arguments. */
+ * tp_layer_bwd(block, rank). ATTN keeps QKV_r [T,3h/t] and the context C_r
+ * [T,h/t] (also in fp32 for bf16); with bf16 and d in {64, 96, 128, 160}
+ * (fused attention) also the bf16 rounding residuals of Q_r and K_r [T,2h/t]
+ * and one log-sum-exp per query and head, otherwise the causal softmax P_r
+ * [b*a_r, s, s]. MLP keeps U_r and Z_r [T,4h/t]. 0 on invalid arguments. */
 size_t tp_saved_bytes(int h, int a, int s, int b, int t, int dtype, int block);
 
 /* Scratch bytes needed by both tp_layer_fwd and tp_layer_bwd of `block`
@@ -136,6 +138,60 @@ int tp_layer_bwd(int h, int a, int s, int b, int t, int rank, int dtype, int blo
  * backward: bias = NULL, residual = the block output's gradient.             */
 int tp_reduce_partials(int dtype, long rows, long cols, int t, const void *partials, const void *bias,
                        const void *residual, void *out, void *stream);
+
+/* Backward with full activation recomputation ("Distributed training"
+ * interview book, section 2.2: full recomputation keeps only the layer input
+ * and pays a second forward pass; paper-graph page, "FLOP Counting and
+ * Training Time Estimation": recomputation adds one forward pass to the
+ * count). Same result as tp_layer_fwd followed by tp_layer_bwd, bit for bit,
+ * without keeping any activation between the two calls:
+ *   scratch  tp_saved_bytes(...) bytes of device memory, overwritten: the
+ *            forward is re-run into it up to (not including) the block's
+ *            output product, whose result the backward does not read; the
+ *            buffer can be shared by every layer, since nothing in it
+ *            outlives the call.
+ * Other arguments, ownership and errors as tp_layer_bwd.                     */
+int tp_layer_bwd_recompute(int h, int a, int s, int b, int t, int rank, int dtype, int block,
+                           const void *x, const tp_block_weights *w, const void *dy, void *dx_partial,
+                           const tp_block_grads *g, void *scratch,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* LayerNorm of `rows` tokens of width h, fused with the bias + residual add
+ * that precedes it. With sequence parallelism ("parallelism" blog post,
+ * "Sequence parallelism: the parts TP leaves behind") a rank runs it on its
+ * own slice of the sequence: between the reduce-scatter that ends one block
+ * and the all-gather that feeds the next, it adds the output bias and the
+ * residual and applies the next LayerNorm.
+ *   v       = x + residual + bias, rounded once to dtype (residual, bias may
+ *             be NULL); written to sum_out [rows, h] if sum_out is not NULL
+ *   y       = (v - mean(v)) / sqrt(var(v) + eps) * gamma + beta, per row,
+ *             mean and biased variance over the h features, in fp32
+ *   stats   [rows, 2] fp32: mean and 1/sqrt(var + eps) of each row
+ * gamma == NULL: add only (then beta, y and stats are not used and sum_out
+ * is required); otherwise beta, y and stats are required.
+ *   x, residual, sum_out, y  [rows, h];  bias, gamma, beta [h]
+ * h must be a multiple of 8 and at most 32768 (bf16) or 16384 (fp32)
+ * (TP_EUNSUPPORTED); eps >= 0. stats needs 8-byte alignment, every other
+ * pointer 16. y and sum_out must not alias the inputs of another row. The page does not write LayerNorm out: this is the textbook
+ * definition.                                                                */
+int tp_layernorm_fwd(int dtype, long rows, long h, float eps, const void *x, const void *bias,
+                     const void *residual, const void *gamma, const void *beta, void *sum_out, void *y,
+                     float *stats, void *stream);
+
+/* Backward of tp_layernorm_fwd for the gradient dy of its output y:
+ *   x_hat = (v - mean) rstd,  g = dy * gamma
+ *   dx     = rstd (g - mean_h(g) - x_hat mean_h(g x_hat)) + dresid
+ *   dgamma = sum over the rows of dy x_hat,  dbeta = sum over the rows of dy
+ *   v      [rows, h] the LayerNorm input (tp_layernorm_fwd's sum_out, or its
+ *          x when no residual or bias was added); stats as written by it
+ *   dresid [rows, h] gradient reaching v through the residual path, or NULL
+ *   dx     [rows, h] out; dgamma, dbeta [h] out, both or neither (NULL).
+ * With sequence parallelism the rows are the rank's own tokens, so dgamma
+ * and dbeta are this rank's partial sums: their sum over the ranks (the
+ * all-reduce of the replicated LayerNorm weights' gradients) is the full
+ * gradient. dx must not alias dy or v.                                       */
+int tp_layernorm_bwd(int dtype, long rows, long h, const void *dy, const void *v, const float *stats,
+                     const void *gamma, const void *dresid, void *dx, void *dgamma, void *dbeta, void *stream);
 
 /* General GEMM on the same MFMA kernels and the same launch planning as the
  * layer's weight GEMMs (whole waves of 256x256 tiles, stream-K over a partial

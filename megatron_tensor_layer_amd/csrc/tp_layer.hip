@@ -39,6 +39,7 @@
 #include "gemm.hpp"
 #include "flash_attn.hpp"
 #include "gemm_direct.hpp"
+#include "layernorm.hpp"
 
 using namespace tpl;
 
@@ -60,7 +61,7 @@ enum Role : int {
   R_FC2_DGRAD, R_FC2_WGRAD, R_DB2, R_FC1_DGRAD, R_FC1_WGRAD, R_DB1,
   R_O_DGRAD, R_O_WGRAD, R_DBO, R_ROWDOT, R_DS, R_DV, R_DQ, R_DK,
   R_QKV_DGRAD, R_QKV_WGRAD, R_DBQKV, R_REDUCE, R_GEMM,
-  R_FC2_BWD, R_FC1_BWD, R_O_BWD, R_QKV_BWD, R_ATT_FWD, R_ATT_DKV, R_ATT_DQ, R_COUNT
+  R_FC2_BWD, R_FC1_BWD, R_O_BWD, R_QKV_BWD, R_ATT_FWD, R_ATT_DKV, R_ATT_DQ, R_LN_FWD, R_LN_BWD, R_COUNT
 };
 
 const char* const kRoleName[R_COUNT] = {
@@ -69,7 +70,7 @@ const char* const kRoleName[R_COUNT] = {
   "o_dgrad", "o_wgrad", "dbo", "rowdot", "ds", "dv", "dq", "dk",
   "qkv_dgrad", "qkv_wgrad", "dbqkv", "reduce", "gemm",
   "fc2_dgrad+wgrad", "fc1_dgrad+wgrad", "o_dgrad+wgrad", "qkv_dgrad+wgrad",
-  "attn_fwd", "attn_dkv", "attn_dq"};
+  "attn_fwd", "attn_dkv", "attn_dq", "ln_fwd", "ln_bwd"};
 
 namespace prof {
 struct Rec {
@@ -586,6 +587,7 @@ char* B8(void* p, size_t off) { return static_cast<char*>(p) + off; }
 const char* B8(const void* p, size_t off) { return static_cast<const char*>(p) + off; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) != 0; }
 
 // Algorithmic cost of one batched attention product over z (sequence, head)
 // pairs: model FLOPs count the full s x s square (Eq. 3 of the paper-graph
@@ -735,7 +737,7 @@ int attn_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, v
     }
   }
   }  // materialised attention
-  {  // partial = C Wo_r
+  if (y) {  // partial = C Wo_r (skipped when the forward is re-run for the backward)
     GemmArgs p = gargs(D.T, D.h, D.hr);
     p.A = C; p.lda = D.hr;
     p.B = w->w_out; p.ldb = D.h;
@@ -876,7 +878,7 @@ int mlp_fwd(const Dims& D, const void* x, const tp_block_weights* w, void* y, vo
     p.bias = w->b_in;
     TRY((linear<true, false, EPI_BIAS_GELU, R_FC1_FWD>(D, p, part, st)));
   }
-  {  // partial = Z W2_r
+  if (y) {  // partial = Z W2_r (skipped when the forward is re-run for the backward)
     GemmArgs p = gargs(D.T, D.h, D.fr);
     p.A = Z; p.lda = D.fr;
     p.B = w->w_out; p.ldb = D.h;
@@ -921,6 +923,58 @@ int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void*
     TRY((pair<EPI_LINEAR, R_FC1_BWD, R_FC1_DGRAD, R_FC1_WGRAD>(D, p, q, part, st)));
   }
   TRY(colsum<R_DB1>(D, dU, g->db_in, D.T, D.fr, D.fr, st));
+  return TP_OK;
+}
+
+// LayerNorm launches: a row takes one wave when it has at most 512 16-byte
+// chunks, else the whole workgroup with NC chunks a thread.
+constexpr long kLnMaxChunks = 256 * 16;
+
+template <typename T>
+hipError_t ln_fwd_launch(const LnFwdArgs& a, hipStream_t st) {
+  const long nch = a.h / Elt<T>::VEC;
+  if (nch <= 64 * 8) {
+    hipLaunchKernelGGL((ln_fwd_kernel<T, 64, 8>), dim3((unsigned)cdivl(a.rows, 4)), dim3(256), 0, st, a);
+  } else {
+    const unsigned g = (unsigned)a.rows;
+    if (nch <= 256 * 4) hipLaunchKernelGGL((ln_fwd_kernel<T, 256, 4>), dim3(g), dim3(256), 0, st, a);
+    else if (nch <= 256 * 8) hipLaunchKernelGGL((ln_fwd_kernel<T, 256, 8>), dim3(g), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((ln_fwd_kernel<T, 256, 16>), dim3(g), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t ln_dparam_launch(const LnBwdArgs& a, hipStream_t st) {
+  constexpr int W = 8 * Elt<T>::VEC;  // columns per workgroup
+  hipLaunchKernelGGL(ln_bwd_dparam_kernel<T>, dim3((unsigned)cdiv(a.h, W)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t ln_bwd_launch(const LnBwdArgs& a, hipStream_t st) {
+  if (a.rows > 0) {
+    const long nch = a.h / Elt<T>::VEC;
+    if (nch <= 64 * 8) {
+      hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 64, 8>), dim3((unsigned)cdivl(a.rows, 4)), dim3(256), 0, st, a);
+    } else {
+      const unsigned g = (unsigned)a.rows;
+      if (nch <= 256 * 4) hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 256, 4>), dim3(g), dim3(256), 0, st, a);
+      else if (nch <= 256 * 8) hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 256, 8>), dim3(g), dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 256, 16>), dim3(g), dim3(256), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // no rows: the parameter gradients are empty sums (zeros)
+  return a.dgamma ? ln_dparam_launch<T>(a, st) : hipSuccess;
+}
+
+// LayerNorm argument checks shared by the two entry points.
+int ln_check(int dtype, long rows, long h) {
+  if (dtype != TP_BF16 && dtype != TP_FP32) return TP_EINVAL;
+  if (rows < 0 || h <= 0) return TP_EINVAL;
+  if (h % 8 != 0 || h / (dtype == TP_BF16 ? 8 : 4) > kLnMaxChunks) return TP_EUNSUPPORTED;
   return TP_OK;
 }
 
@@ -1001,6 +1055,69 @@ int tp_reduce_partials(int dtype, long rows, long cols, int t, const void* parti
                        (const float*)bias, (const float*)residual, (float*)out, rows, cols, t);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? TP_OK : hip_fail(e);
+}
+
+int tp_layernorm_fwd(int dtype, long rows, long h, float eps, const void* x, const void* bias, const void* residual,
+                     const void* gamma, const void* beta, void* sum_out, void* y, float* stats, void* stream) {
+  int rc = ln_check(dtype, rows, h);
+  if (rc != TP_OK) return rc;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_EINVAL;
+  if (rows == 0) return TP_OK;  // no tokens: nothing is read or written
+  if (!x) return TP_ENULL;
+  if (gamma ? (!beta || !y || !stats) : !sum_out) return TP_ENULL;
+  if (misaligned(x) || misaligned(bias) || misaligned(residual) || misaligned(gamma) || misaligned(beta) ||
+      misaligned(sum_out) || misaligned(y) || misaligned8(stats))
+    return TP_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  LnFwdArgs a{x, bias, residual, gamma, beta, sum_out, gamma ? y : nullptr, gamma ? stats : nullptr,
+              rows, (int)h, eps};
+  const double es = dtype == TP_BF16 ? 2.0 : 4.0, n = (double)rows * h;
+  const double bytes = es * n * (1 + (residual ? 1 : 0) + (sum_out ? 1 : 0) + (gamma ? 1 : 0)) +
+                       es * h * ((bias ? 1 : 0) + (gamma ? 2 : 0)) + (gamma ? 8.0 * rows : 0.0);
+  prof::Scope sc(R_LN_FWD, 0.0, bytes, st);
+  hipError_t e = dtype == TP_BF16 ? ln_fwd_launch<bf16_t>(a, st) : ln_fwd_launch<float>(a, st);
+  return e == hipSuccess ? TP_OK : hip_fail(e);
+}
+
+int tp_layernorm_bwd(int dtype, long rows, long h, const void* dy, const void* v, const float* stats,
+                     const void* gamma, const void* dresid, void* dx, void* dgamma, void* dbeta, void* stream) {
+  int rc = ln_check(dtype, rows, h);
+  if (rc != TP_OK) return rc;
+  if ((!dgamma) != (!dbeta)) return TP_ENULL;
+  if (rows > 0 && (!dy || !v || !stats || !gamma || !dx)) return TP_ENULL;  // no tokens: only dgamma, dbeta
+  if (misaligned(dy) || misaligned(v) || misaligned8(stats) || misaligned(gamma) || misaligned(dresid) ||
+      misaligned(dx) || misaligned(dgamma) || misaligned(dbeta))
+    return TP_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const double es = dtype == TP_BF16 ? 2.0 : 4.0, n = (double)rows * h;
+  const double bytes = es * n * (3 + (dresid ? 1 : 0)) + es * h * (1 + (dgamma ? 2 : 0)) + 8.0 * rows;
+  prof::Scope sc(R_LN_BWD, 0.0, bytes, st);
+  LnBwdArgs a{dy, v, gamma, dresid, stats, dx, dgamma, dbeta, rows, (int)h};
+  hipError_t e = dtype == TP_BF16 ? ln_bwd_launch<bf16_t>(a, st) : ln_bwd_launch<float>(a, st);
+  return e == hipSuccess ? TP_OK : hip_fail(e);
+}
+
+int tp_layer_bwd_recompute(int h, int a, int s, int b, int t, int rank, int dtype, int block, const void* x,
+                           const tp_block_weights* w, const void* dy, void* dx_partial, const tp_block_grads* g,
+                           void* scratch, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_args(h, a, s, b, t, rank, dtype, block);
+  if (rc != TP_OK) return rc;
+  if (!x || !w || !w->w_in || !w->b_in || !w->w_out || !dy || !dx_partial || !g || !g->dw_in || !g->db_in ||
+      !g->dw_out || !g->db_out || !scratch || !workspace)
+    return TP_ENULL;
+  if (misaligned(x) || misaligned(w->w_in) || misaligned(w->b_in) || misaligned(w->w_out) || misaligned(dy) ||
+      misaligned(dx_partial) || misaligned(g->dw_in) || misaligned(g->db_in) || misaligned(g->dw_out) ||
+      misaligned(g->db_out) || misaligned(scratch) || misaligned(workspace))
+    return TP_EALIGN;
+  const Dims D = make_dims(h, a, s, b, t, dtype);
+  if (workspace_bytes < ws_layout(D, block).total) return TP_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the forward again, up to (not including) the block's output product, into scratch
+  rc = block == TP_ATTN ? attn_fwd(D, x, w, nullptr, scratch, workspace, st)
+                        : mlp_fwd(D, x, w, nullptr, scratch, workspace, st);
+  if (rc != TP_OK) return rc;
+  return block == TP_ATTN ? attn_bwd(D, x, w, scratch, dy, dx_partial, g, workspace, st)
+                          : mlp_bwd(D, x, w, scratch, dy, dx_partial, g, workspace, st);
 }
 
 size_t tp_gemm_workspace_bytes(int dtype, int M, int N, int K) {

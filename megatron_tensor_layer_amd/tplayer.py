@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtplayer.
 
 # every symbol include/tp_layer.h declares
 EXPORTS = ("tp_check_args", "tp_saved_bytes", "tp_workspace_bytes", "tp_layer_fwd", "tp_layer_bwd",
-           "tp_reduce_partials", "tp_gemm_workspace_bytes", "tp_gemm", "tp_prof_enable", "tp_prof_read", "tp_strerror")
+           "tp_reduce_partials", "tp_layer_bwd_recompute", "tp_layernorm_fwd", "tp_layernorm_bwd",
+           "tp_gemm_workspace_bytes", "tp_gemm", "tp_prof_enable", "tp_prof_read", "tp_strerror")
 
 _lib = None
 
@@ -70,6 +71,13 @@ def lib():
     L.tp_layer_bwd.restype = i
     L.tp_reduce_partials.argtypes = [i, lng, lng, i, vp, vp, vp, vp, vp]
     L.tp_reduce_partials.restype = i
+    L.tp_layer_bwd_recompute.argtypes = dims + [vp, ctypes.POINTER(TPBlockWeights), vp, vp,
+                                                ctypes.POINTER(TPBlockGrads), vp, vp, sz, vp]
+    L.tp_layer_bwd_recompute.restype = i
+    L.tp_layernorm_fwd.argtypes = [i, lng, lng, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.tp_layernorm_fwd.restype = i
+    L.tp_layernorm_bwd.argtypes = [i, lng, lng, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.tp_layernorm_bwd.restype = i
     L.tp_prof_enable.argtypes, L.tp_prof_enable.restype = [i], i
     L.tp_prof_read.argtypes, L.tp_prof_read.restype = [ctypes.POINTER(TPProfEntry), i], i
     L.tp_gemm_workspace_bytes.argtypes = [i, i, i, i]
@@ -182,6 +190,55 @@ def tp_reduce_partials(dtype, partials, out, bias=None, residual=None, stream=No
     _expect(residual, rows * cols, dt, "residual")
     _check(lib().tp_reduce_partials(dtype, rows, cols, t, _ptr(partials), _ptr(bias), _ptr(residual), _ptr(out),
                                     _stream(stream)), "tp_reduce_partials")
+
+
+def tp_layer_bwd_recompute(h, a, s, b, t, rank, dtype, block, x, w, dy, dx_partial, g, scratch, workspace,
+                           stream=None):
+    """tp_layer_bwd that re-runs the forward into `scratch` (tp_saved_bytes) first."""
+    dt = torch_dtype(dtype)
+    T = s * b
+    shapes = block_shapes(h, t, block)
+    for name, tens, shp in zip(("w_in", "b_in", "w_out", "b_out"), w, shapes):
+        _expect(tens, int(torch.Size(shp).numel()), dt, name)
+    for name, tens, shp in zip(("dw_in", "db_in", "dw_out", "db_out"), g, shapes):
+        _expect(tens, int(torch.Size(shp).numel()), dt, name)
+    _expect(x, T * h, dt, "x")
+    _expect(dy, T * h, dt, "dy")
+    _expect(dx_partial, T * h, dt, "dx_partial")
+    if scratch.numel() * scratch.element_size() < tp_saved_bytes(h, a, s, b, t, dtype, block):
+        raise ValueError("scratch: smaller than tp_saved_bytes")
+    W = TPBlockWeights(*[t_.data_ptr() for t_ in w])
+    G = TPBlockGrads(*[t_.data_ptr() for t_ in g])
+    rc = lib().tp_layer_bwd_recompute(h, a, s, b, t, rank, dtype, block, _ptr(x), ctypes.byref(W), _ptr(dy),
+                                      _ptr(dx_partial), ctypes.byref(G), _ptr(scratch), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "tp_layer_bwd_recompute")
+
+
+def tp_layernorm_fwd(dtype, x, gamma=None, beta=None, y=None, stats=None, bias=None, residual=None, sum_out=None,
+                     eps=1e-5, stream=None):
+    """v = x + residual + bias (into sum_out); y = LayerNorm(v) gamma + beta, stats [rows, 2] fp32."""
+    rows, h = x.shape
+    dt = torch_dtype(dtype)
+    _expect(x, rows * h, dt, "x")
+    for name, tens, n in (("bias", bias, h), ("residual", residual, rows * h), ("gamma", gamma, h),
+                          ("beta", beta, h), ("sum_out", sum_out, rows * h), ("y", y, rows * h)):
+        _expect(tens, n, dt, name)
+    _expect(stats, rows * 2, torch.float32, "stats")
+    _check(lib().tp_layernorm_fwd(dtype, rows, h, eps, _ptr(x), _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(beta),
+                                  _ptr(sum_out), _ptr(y), _ptr(stats), _stream(stream)), "tp_layernorm_fwd")
+
+
+def tp_layernorm_bwd(dtype, dy, v, stats, gamma, dx, dresid=None, dgamma=None, dbeta=None, stream=None):
+    """dx = LayerNorm backward of dy (+ dresid); dgamma, dbeta = sums over the rows."""
+    rows, h = dy.shape
+    dt = torch_dtype(dtype)
+    for name, tens, n in (("dy", dy, rows * h), ("v", v, rows * h), ("gamma", gamma, h), ("dx", dx, rows * h),
+                          ("dresid", dresid, rows * h), ("dgamma", dgamma, h), ("dbeta", dbeta, h)):
+        _expect(tens, n, dt, name)
+    _expect(stats, rows * 2, torch.float32, "stats")
+    _check(lib().tp_layernorm_bwd(dtype, rows, h, _ptr(dy), _ptr(v), _ptr(stats), _ptr(gamma), _ptr(dresid),
+                                  _ptr(dx), _ptr(dgamma), _ptr(dbeta), _stream(stream)), "tp_layernorm_bwd")
 
 
 def tp_prof_enable(on: bool):

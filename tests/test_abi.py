@@ -147,3 +147,54 @@ def test_strerror():
     for code in (tp.TP_OK, tp.TP_EINVAL, tp.TP_EUNSUPPORTED, tp.TP_ENULL, tp.TP_EALIGN, tp.TP_EWORKSPACE, tp.TP_EHIP):
         assert len(tp.strerror(code)) > 0
     assert "unknown" in tp.strerror(-99)
+
+
+def test_layernorm_validation_on_host():
+    L = tp.lib()
+    a = _fake(0x100000)
+    none = ctypes.c_void_p(None)
+    BF, F32 = tp.TP_BF16, tp.TP_FP32
+    f = L.tp_layernorm_fwd
+    # dtype, sizes, eps
+    assert f(7, 4, 64, 1e-5, a, none, none, a, a, none, a, a, None) == tp.TP_EINVAL
+    assert f(BF, -1, 64, 1e-5, a, none, none, a, a, none, a, a, None) == tp.TP_EINVAL
+    assert f(BF, 4, 0, 1e-5, a, none, none, a, a, none, a, a, None) == tp.TP_EINVAL
+    assert f(BF, 4, 60, 1e-5, a, none, none, a, a, none, a, a, None) == tp.TP_EUNSUPPORTED  # h % 8
+    assert f(BF, 4, 32776, 1e-5, a, none, none, a, a, none, a, a, None) == tp.TP_EUNSUPPORTED
+    assert f(F32, 4, 16392, 1e-5, a, none, none, a, a, none, a, a, None) == tp.TP_EUNSUPPORTED
+    assert f(BF, 4, 64, -1.0, a, none, none, a, a, none, a, a, None) == tp.TP_EINVAL
+    assert f(BF, 4, 64, float("nan"), a, none, none, a, a, none, a, a, None) == tp.TP_EINVAL
+    # required pointers: with gamma, beta + y + stats; without gamma, sum_out
+    assert f(BF, 4, 64, 1e-5, none, none, none, a, a, none, a, a, None) == tp.TP_ENULL
+    assert f(BF, 4, 64, 1e-5, a, none, none, a, none, none, a, a, None) == tp.TP_ENULL
+    assert f(BF, 4, 64, 1e-5, a, none, none, a, a, none, a, none, None) == tp.TP_ENULL
+    assert f(BF, 4, 64, 1e-5, a, a, a, none, none, none, none, none, None) == tp.TP_ENULL
+    # alignment: 16 bytes, stats 8
+    assert f(BF, 4, 64, 1e-5, _fake(0x100008), none, none, a, a, none, a, a, None) == tp.TP_EALIGN
+    assert f(BF, 4, 64, 1e-5, a, none, none, a, a, none, a, _fake(0x100004), None) == tp.TP_EALIGN
+    # zero rows: nothing to do, no pointer needed
+    assert f(BF, 0, 64, 1e-5, none, none, none, none, none, none, none, none, None) == tp.TP_OK
+    b = L.tp_layernorm_bwd
+    assert b(BF, 4, 64, a, a, a, a, none, a, a, none, None) == tp.TP_ENULL            # dgamma without dbeta
+    assert b(BF, 4, 64, none, a, a, a, none, a, none, none, None) == tp.TP_ENULL      # no dy
+    assert b(BF, 4, 64, a, a, a, none, none, a, none, none, None) == tp.TP_ENULL      # no gamma
+    assert b(BF, 4, 64, a, a, _fake(0x100004), a, none, a, none, none, None) == tp.TP_EALIGN
+    assert b(BF, 4, 64, a, a, a, a, _fake(0x100002), a, none, none, None) == tp.TP_EALIGN
+    assert b(BF, 4, 61, a, a, a, a, none, a, none, none, None) == tp.TP_EUNSUPPORTED
+    assert b(BF, 0, 64, none, none, none, none, none, none, none, none, None) == tp.TP_OK
+
+
+def test_recompute_validation_on_host():
+    L = tp.lib()
+    dims = (64, 4, 32, 2, 4, 1, tp.TP_FP32, tp.TP_MLP)
+    ok = tp.TPBlockWeights(0x10000, 0x20000, 0x30000, 0x40000)
+    g = tp.TPBlockGrads(0x50000, 0x60000, 0x70000, 0x80000)
+    a = _fake(0x100000)
+    none = ctypes.c_void_p(None)
+    ws = tp.tp_workspace_bytes(64, 4, 32, 2, 4, tp.TP_FP32, tp.TP_MLP)
+    f = L.tp_layer_bwd_recompute
+    assert f(*dims, a, ctypes.byref(ok), a, a, ctypes.byref(g), none, a, ws, None) == tp.TP_ENULL     # scratch
+    assert f(*dims, a, ctypes.byref(ok), a, a, ctypes.byref(g), _fake(0x100008), a, ws, None) == tp.TP_EALIGN
+    assert f(*dims, a, ctypes.byref(ok), a, a, ctypes.byref(g), a, a, ws - 1, None) == tp.TP_EWORKSPACE
+    assert f(64, 4, 32, 2, 3, 0, tp.TP_FP32, tp.TP_MLP, a, ctypes.byref(ok), a, a, ctypes.byref(g), a, a, ws,
+             None) == tp.TP_EINVAL
