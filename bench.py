@@ -17,7 +17,14 @@ share:
 Inputs are synthetic and seeded: weights and biases N(0, 0.02^2), X and dY
 N(0, 1), drawn on the GPU by torch's generator and stored in bf16.
 
-    python bench.py [--steps K] [--warmup W] [--config gpt_175b] [--no-cpu-baseline]
+Two more forms of the same layer are timed beside it and reported as objects
+of the same line: the pre-norm layer with sequence parallelism (LayerNorm,
+bias and residual on each rank's T/t tokens; "sequence_parallel_layernorm")
+and the backward with full activation recomputation ("recompute", counted
+with the page's 96 b s h^2 (1 + s/6h) per layer as well as by executed
+products).
+
+    python bench.py [--steps K] [--warmup W] [--config gpt_175b] [--no-cpu-baseline] [--no-modes]
 
 Prints one JSON line.  Only one GPU is used: --gpus above 1 is refused.
 """
@@ -158,6 +165,147 @@ def timed_steps(layer, X, dY, steps):
     return seg, wall
 
 
+def segment_times(steps, segs):
+    """Run `steps` passes of the (fn, counted) segments with HIP events
+    (torch's current stream, the library's stream) around each; returns the
+    per-step milliseconds of the counted and of the other segments."""
+    import torch
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(segs) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record()
+        for i, (fn, _) in enumerate(segs):
+            fn()
+            ev[k][i + 1].record()
+    torch.cuda.synchronize()
+    counted, other, per_seg = [], [], [0.0] * len(segs)
+    for k in range(steps):
+        c = o = 0.0
+        for i, (_, cnt) in enumerate(segs):
+            ms = ev[k][i].elapsed_time(ev[k][i + 1])
+            per_seg[i] += ms / steps
+            if cnt:
+                c += ms
+            else:
+                o += ms
+        counted.append(c)
+        other.append(o)
+    return counted, other, per_seg
+
+
+def recompute_flops_per_rank(cfg):
+    """Matmul FLOPs the recomputing backward re-runs per rank: the QKV and FC1
+    products and the two attention products of the forward (the output
+    products are not re-run: the backward does not read their results)."""
+    h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    T = s * b
+    return 2.0 * T * h * (3 * h // t) + 2.0 * T * h * (4 * h // t) + 2 * 2.0 * b * (a // t) * s * s * (h // a)
+
+
+def measure_recompute(layer, X, dY, cfg, steps, warmup):
+    """The layer with full activation recomputation: forward of both blocks
+    keeps nothing, each backward re-runs its block's forward first."""
+    import numpy as np
+    from megatron_tensor_layer_amd import tplayer as tp
+    from megatron_tensor_layer_amd.layer import TPLayer
+
+    h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    rl = TPLayer(h, a, s, b, t, tp.TP_BF16, layer.weights, recompute=True)
+    for _ in range(warmup):
+        rl.forward(X)
+        rl.backward(dY)
+    segs = [(lambda: [rl.block_fwd(tp.TP_ATTN, r, X, rl.partials[r]) for r in range(t)], True),
+            (lambda: rl.reduce(rl.H, rl.weights[0]["attn"][3], X), False),
+            (lambda: [rl.block_fwd(tp.TP_MLP, r, rl.H, rl.partials[r]) for r in range(t)], True),
+            (lambda: rl.reduce(rl.Y, rl.weights[0]["mlp"][3], rl.H), False),
+            (lambda: [rl.block_bwd(tp.TP_MLP, r, rl.H, dY, rl.partials[r]) for r in range(t)], True),
+            (lambda: rl.reduce(rl.dH, None, dY), False),
+            (lambda: [rl.block_bwd(tp.TP_ATTN, r, X, rl.dH, rl.partials[r]) for r in range(t)], True),
+            (lambda: rl.reduce(rl.dX, None, rl.dH), False)]
+    counted, _, _ = segment_times(steps, segs)
+    t_rank = float(np.mean(counted)) / t
+    F = model_flops_per_rank(h, s, b, t)
+    F96 = F * 96.0 / 72.0
+    Fx = F + recompute_flops_per_rank(cfg)
+    saved_bytes = sum(tp.tp_saved_bytes(h, a, s, b, t, tp.TP_BF16, blk) for blk in (tp.TP_ATTN, tp.TP_MLP))
+    out = {"rank_ms": round(t_rank, 4),
+           "model_tflops_96": round(F96 / (t_rank * 1e-3) / 1e12, 1),
+           "pct_of_peak_96": round(100.0 * F96 / (t_rank * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "executed_tflops": round(Fx / (t_rank * 1e-3) / 1e12, 1),
+           "flops_per_rank_96": F96, "flops_per_rank_executed": Fx,
+           "activation_bytes_kept_per_rank_layer": 0, "activation_bytes_kept_without_recompute": saved_bytes,
+           "scratch_bytes_shared": int(rl.scratch.numel()),
+           "accounting": "model TFLOP/s with the paper-graph page's 96 b s h^2 (1 + s/6h) per layer (one extra "
+                         "forward counted in full); executed counts the products actually re-run"}
+    del rl
+    return out
+
+
+def measure_sequence_parallel(layer, X, dY, cfg, steps, warmup):
+    """The pre-norm layer with sequence parallelism: LayerNorms, output
+    biases and residual adds on each rank's T/t tokens (rank work), the
+    stand-in sums between them (not counted)."""
+    import numpy as np
+    import torch
+    from megatron_tensor_layer_amd import tplayer as tp
+    from megatron_tensor_layer_amd.layer import SPLayer
+
+    h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    ln = ((1.0 + 0.1 * torch.randn(h, generator=g, device="cuda")).to(torch.bfloat16),
+          (0.02 * torch.randn(h, generator=g, device="cuda")).to(torch.bfloat16),
+          (1.0 + 0.1 * torch.randn(h, generator=g, device="cuda")).to(torch.bfloat16),
+          (0.02 * torch.randn(h, generator=g, device="cuda")).to(torch.bfloat16))
+    sp = SPLayer(h, a, s, b, t, tp.TP_BF16, layer.weights, ln)
+    for _ in range(warmup):
+        sp.forward(X)
+        sp.backward(dY)
+    R = range(t)
+    segs = [(lambda: [sp.ln1_fwd(r, X) for r in R], True),
+            (lambda: [sp.block_fwd(tp.TP_ATTN, r, sp.A, sp.partials[r]) for r in R], True),
+            (sp.reduce_sum, False),
+            (lambda: [sp.add_ln2_fwd(r, X) for r in R], True),
+            (lambda: [sp.block_fwd(tp.TP_MLP, r, sp.B, sp.partials[r]) for r in R], True),
+            (sp.reduce_sum, False),
+            (lambda: [sp.add_out_fwd(r) for r in R], True),
+            (lambda: [sp.block_bwd(tp.TP_MLP, r, sp.B, dY, sp.partials[r]) for r in R], True),
+            (sp.reduce_sum, False),
+            (lambda: [sp.ln2_bwd(r, dY) for r in R], True),
+            (lambda: [sp.block_bwd(tp.TP_ATTN, r, sp.A, sp.dH, sp.partials[r]) for r in R], True),
+            (sp.reduce_sum, False),
+            (lambda: [sp.ln1_bwd(r, X) for r in R], True),
+            (sp.reduce_ln_grads, False)]
+    counted, other, per_seg = segment_times(steps, segs)
+    t_rank = float(np.mean(counted)) / t
+    F = model_flops_per_rank(h, s, b, t)
+    # LayerNorm calls: each segment holds the t ranks' launches of one call;
+    # algorithmic bytes: every [T/t, h] operand once, the [h] vectors once,
+    # 8 bytes of statistics per row
+    n, es = s * b // t, 2.0
+    calls = {"ln1_fwd (LN1 of the block input)": (0, es * (2 * n * h + 2 * h) + 8 * n),
+             "add_ln2_fwd (bias + residual + LN2)": (3, es * (4 * n * h + 3 * h) + 8 * n),
+             "add_out_fwd (bias + residual)": (6, es * (3 * n * h + h)),
+             "ln2_bwd (dx + residual grad, dgamma, dbeta)": (9, es * (4 * n * h + 3 * h) + 8 * n),
+             "ln1_bwd (dx + residual grad, dgamma, dbeta)": (12, es * (4 * n * h + 3 * h) + 8 * n)}
+    kernels = {}
+    for name, (i, nbytes) in calls.items():
+        ms = per_seg[i] / t
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        kernels[name] = {"ms_per_call": round(ms, 5), "bound": "hbm", "achieved": round(gbps, 1),
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                         "algorithmic_bytes": nbytes}
+    out = {"rank_ms": round(t_rank, 4), "model_tflops": round(F / (t_rank * 1e-3) / 1e12, 1),
+           "pct_of_peak": round(100.0 * F / (t_rank * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "rows_per_rank": s * b // t, "standin_ms_per_step": round(float(np.mean(other)), 4),
+           "layernorm_calls": kernels,
+           "layernorm_ms_per_rank": round(sum(per_seg[i] for i, _ in calls.values()) / t, 4),
+           "note": "pre-norm layer: the same products plus LayerNorm fwd/bwd, bias and residual on T/t rows"}
+    del sp
+    return out
+
+
 def cpu_baseline(cfg, target_s=15.0):
     """The fp64 oracle (as it stands) on a bounded sample of the same
     workload: rank 0's share of the layer, forward + backward of both blocks,
@@ -207,6 +355,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the sequence-parallel LayerNorm and recompute measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the t tensor-parallel ranks "
@@ -291,6 +441,10 @@ def main():
         "roles": roles,
         "context": "pages: 163 TFLOP/s per A100 (52% of 312) end-to-end with recompute; not this metric",
     }
+    if not args.no_modes:
+        n = max(3, args.steps // 2)
+        out["sequence_parallel_layernorm"] = measure_sequence_parallel(layer, X, dY, cfg, n, 1)
+        out["recompute"] = measure_recompute(layer, X, dY, cfg, n, 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     else:

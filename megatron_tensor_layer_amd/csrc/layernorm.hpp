@@ -13,7 +13,7 @@
 //             dgamma = sum over rows of dy x_hat, dbeta = sum over rows of dy
 //
 // Bandwidth-bound: each row is read once into registers (packed, 16 bytes a
-// chunk) and both reductions over the row run on the registers. TPR threads
+// chunk) and the reductions over the row run on the registers. TPR threads
 // share a row: one wave for rows of up to 512 chunks (h <= 4096 in bf16), else
 // the whole 256-thread workgroup. Reductions are fixed trees (wave butterfly,
 // then the four waves in order), so results do not depend on timing.
@@ -42,19 +42,58 @@ struct LnBwdArgs {
 
 namespace ln {
 
-// Sum over the TPR threads of a row; every thread gets the same value.
+// Sums of two values over the TPR threads of a row; every thread gets the
+// same pair (a butterfly adds the same two partials on both partners).
 template <int TPR>
-__device__ __forceinline__ float row_sum(float v, float* red) {
+__device__ __forceinline__ float2 row_sum2(float2 v, float2* red) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 32; o >= 1; o >>= 1) {
+    v.x += __shfl_xor(v.x, o, 64);
+    v.y += __shfl_xor(v.y, o, 64);
+  }
   if constexpr (TPR == 64) {
     return v;
   } else {
     static_assert(TPR == 256, "a row takes one wave or the whole workgroup");
-    __syncthreads();  // the previous reduction has read red
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    return make_float2((red[0].x + red[1].x) + (red[2].x + red[3].x), (red[0].y + red[1].y) + (red[2].y + red[3].y));
+  }
+}
+
+// Count, mean and sum of squared deviations of each thread's values,
+// combined over the row's TPR threads by the pairwise update of Chan, Golub
+// and LeVeque (n = na + nb, mean = (na ma + nb mb) / n,
+// M2 = M2a + M2b + (mb - ma)^2 na nb / n), written symmetrically in the two
+// partners so that every thread ends with bit-identical moments. One
+// reduction round: the variance needs no second pass over the row.
+__device__ __forceinline__ void chan_merge(float& n, float& m, float& q, float nb, float mb, float qb) {
+  const float nn = n + nb;
+  if (nn > 0.0f) {
+    const float d = mb - m;
+    const float mm = (n * m + nb * mb) / nn;
+    q = (q + qb) + d * d * (n * nb / nn);
+    m = mm;
+  }
+  n = nn;
+}
+
+template <int TPR>
+__device__ __forceinline__ void row_moments(float& n, float& m, float& q, float4* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float nb = __shfl_xor(n, o, 64), mb = __shfl_xor(m, o, 64), qb = __shfl_xor(q, o, 64);
+    chan_merge(n, m, q, nb, mb, qb);
+  }
+  if constexpr (TPR == 256) {
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float4(n, m, q, 0.0f);
+    __syncthreads();
+    float n0 = red[0].x, m0 = red[0].y, q0 = red[0].z;
+    float n2 = red[2].x, m2 = red[2].y, q2 = red[2].z;
+    chan_merge(n0, m0, q0, red[1].x, red[1].y, red[1].z);
+    chan_merge(n2, m2, q2, red[3].x, red[3].y, red[3].z);
+    chan_merge(n0, m0, q0, n2, m2, q2);
+    n = n0; m = m0; q = q0;
   }
 }
 
@@ -72,11 +111,13 @@ __device__ __forceinline__ uint4 pack(const float f[Elt<T>::VEC]) {
 
 }  // namespace ln
 
-// One row per TPR threads; NC = most 16-byte chunks a thread holds.
+// One row per TPR threads; NC = most 16-byte chunks a thread holds. Every
+// load of the row (and of bias, gamma, beta) is issued before the first
+// reduction, so the row costs one memory round trip and one barrier round.
 template <typename T, int TPR, int NC>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const LnFwdArgs a) {
   constexpr int VEC = Elt<T>::VEC, RPW = 256 / TPR;
-  __shared__ float red[4];
+  __shared__ float4 red[4];
   const long row = (long)blockIdx.x * RPW + threadIdx.x / TPR;
   const int lane = threadIdx.x % TPR;
   if (row >= a.rows) return;  // only with TPR = 64, whose reductions need no barrier
@@ -85,23 +126,38 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const LnFwdArgs a) {
   const T* x = static_cast<const T*>(a.x) + base;
   const T* rs = a.resid ? static_cast<const T*>(a.resid) + base : nullptr;
   const T* bs = static_cast<const T*>(a.bias);
-  uint4 pv[NC];
-  float s = 0.0f;
+  const T* gm = static_cast<const T*>(a.gamma);
+  const T* bt = static_cast<const T*>(a.beta);
+  uint4 pv[NC], pr[NC], pb[NC], pg[NC], pt[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = lane + c * TPR;
+    if (ch < nch) {
+      pv[c] = *reinterpret_cast<const uint4*>(x + ch * VEC);
+      if (rs) pr[c] = *reinterpret_cast<const uint4*>(rs + ch * VEC);
+      if (bs) pb[c] = *reinterpret_cast<const uint4*>(bs + ch * VEC);
+      if (gm) {
+        pg[c] = *reinterpret_cast<const uint4*>(gm + ch * VEC);
+        pt[c] = *reinterpret_cast<const uint4*>(bt + ch * VEC);
+      }
+    }
+  }
+  float cnt = 0.0f, s = 0.0f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = lane + c * TPR;
     if (ch < nch) {
       float v[VEC];
-      loadv<T, VEC>(x + ch * VEC, v);
+      ln::unpack<T>(pv[c], v);
       if (rs) {
         float r[VEC];
-        loadv<T, VEC>(rs + ch * VEC, r);
+        ln::unpack<T>(pr[c], r);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) v[e] += r[e];
       }
       if (bs) {
         float b[VEC];
-        loadv<T, VEC>(bs + ch * VEC, b);
+        ln::unpack<T>(pb[c], b);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) v[e] += b[e];
       }
@@ -110,12 +166,12 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const LnFwdArgs a) {
       ln::unpack<T>(pv[c], v);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) s += v[e];
+      cnt += (float)VEC;
     }
   }
-  if (!a.gamma) return;  // add only (uniform over the workgroup)
-  const float inv_h = 1.0f / (float)a.h;
-  const float mean = ln::row_sum<TPR>(s, red) * inv_h;
-  float q = 0.0f;
+  if (!gm) return;  // add only (uniform over the workgroup)
+  // this thread's mean and squared deviations, then the row's
+  float m = cnt > 0.0f ? s / cnt : 0.0f, q = 0.0f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (lane + c * TPR < nch) {
@@ -123,15 +179,13 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const LnFwdArgs a) {
       ln::unpack<T>(pv[c], v);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float dv = v[e] - mean;
+        const float dv = v[e] - m;
         q += dv * dv;
       }
     }
   }
-  const float var = ln::row_sum<TPR>(q, red) * inv_h;
-  const float rstd = 1.0f / sqrtf(var + a.eps);
-  const T* gm = static_cast<const T*>(a.gamma);
-  const T* bt = static_cast<const T*>(a.beta);
+  ln::row_moments<TPR>(cnt, m, q, red);
+  const float mean = m, rstd = 1.0f / sqrtf(q / (float)a.h + a.eps);
   T* y = static_cast<T*>(a.y) + base;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -139,57 +193,63 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const LnFwdArgs a) {
     if (ch < nch) {
       float v[VEC], g[VEC], b[VEC];
       ln::unpack<T>(pv[c], v);
-      loadv<T, VEC>(gm + ch * VEC, g);
-      loadv<T, VEC>(bt + ch * VEC, b);
+      ln::unpack<T>(pg[c], g);
+      ln::unpack<T>(pt[c], b);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) v[e] = (v[e] - mean) * rstd * g[e] + b[e];
       storev<T, VEC>(y + ch * VEC, v);
     }
   }
-  if (lane == 0) {
-    a.stats[2 * row] = mean;
-    a.stats[2 * row + 1] = rstd;
-  }
+  if (lane == 0) *reinterpret_cast<float2*>(a.stats + 2 * row) = make_float2(mean, rstd);
 }
 
-// dx of one row per TPR threads.
+// dx of one row per TPR threads: all loads first, one barrier round for
+// the two row sums.
 template <typename T, int TPR, int NC>
 __global__ void __launch_bounds__(256) ln_bwd_dx_kernel(const LnBwdArgs a) {
   constexpr int VEC = Elt<T>::VEC, RPW = 256 / TPR;
-  __shared__ float red[4];
+  __shared__ float2 red[4];
   const long row = (long)blockIdx.x * RPW + threadIdx.x / TPR;
   const int lane = threadIdx.x % TPR;
   if (row >= a.rows) return;
   const int nch = a.h / VEC;
   const long base = row * a.h;
-  const float mean = a.stats[2 * row], rstd = a.stats[2 * row + 1];
+  const float2 st = *reinterpret_cast<const float2*>(a.stats + 2 * row);
+  const float mean = st.x, rstd = st.y;
   const T* dy = static_cast<const T*>(a.dy) + base;
   const T* vv = static_cast<const T*>(a.v) + base;
   const T* gm = static_cast<const T*>(a.gamma);
-  uint4 pd[NC], pv[NC];
-  float s1 = 0.0f, s2 = 0.0f;
+  const T* dr = a.dresid ? static_cast<const T*>(a.dresid) + base : nullptr;
+  uint4 pd[NC], pv[NC], pg[NC], pr[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = lane + c * TPR;
     if (ch < nch) {
       pd[c] = *reinterpret_cast<const uint4*>(dy + ch * VEC);
       pv[c] = *reinterpret_cast<const uint4*>(vv + ch * VEC);
+      pg[c] = *reinterpret_cast<const uint4*>(gm + ch * VEC);
+      if (dr) pr[c] = *reinterpret_cast<const uint4*>(dr + ch * VEC);
+    }
+  }
+  float2 sum = make_float2(0.0f, 0.0f);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (lane + c * TPR < nch) {
       float d[VEC], v[VEC], g[VEC];
       ln::unpack<T>(pd[c], d);
       ln::unpack<T>(pv[c], v);
-      loadv<T, VEC>(gm + ch * VEC, g);
+      ln::unpack<T>(pg[c], g);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float gg = d[e] * g[e];
-        s1 += gg;
-        s2 += gg * ((v[e] - mean) * rstd);
+        sum.x += gg;
+        sum.y += gg * ((v[e] - mean) * rstd);
       }
     }
   }
+  const float2 tot = ln::row_sum2<TPR>(sum, red);
   const float inv_h = 1.0f / (float)a.h;
-  const float m1 = ln::row_sum<TPR>(s1, red) * inv_h;
-  const float m2 = ln::row_sum<TPR>(s2, red) * inv_h;
-  const T* dr = a.dresid ? static_cast<const T*>(a.dresid) + base : nullptr;
+  const float m1 = tot.x * inv_h, m2 = tot.y * inv_h;
   T* dx = static_cast<T*>(a.dx) + base;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -198,7 +258,7 @@ __global__ void __launch_bounds__(256) ln_bwd_dx_kernel(const LnBwdArgs a) {
       float d[VEC], v[VEC], g[VEC], o[VEC];
       ln::unpack<T>(pd[c], d);
       ln::unpack<T>(pv[c], v);
-      loadv<T, VEC>(gm + ch * VEC, g);
+      ln::unpack<T>(pg[c], g);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float xh = (v[e] - mean) * rstd;
@@ -206,7 +266,7 @@ __global__ void __launch_bounds__(256) ln_bwd_dx_kernel(const LnBwdArgs a) {
       }
       if (dr) {
         float r[VEC];
-        loadv<T, VEC>(dr + ch * VEC, r);
+        ln::unpack<T>(pr[c], r);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) o[e] += r[e];
       }
@@ -226,17 +286,33 @@ __global__ void __launch_bounds__(256) ln_bwd_dparam_kernel(const LnBwdArgs a) {
 #pragma unroll
   for (int e = 0; e < VEC; ++e) ag[e] = ab[e] = 0.0f;
   if (col < a.h) {
+    constexpr int U = 8;  // rows in flight per thread
     const T* dy = static_cast<const T*>(a.dy) + col;
     const T* vv = static_cast<const T*>(a.v) + col;
-    for (long r = rg; r < a.rows; r += RG) {
-      float d[VEC], v[VEC];
-      loadv<T, VEC>(dy + r * a.h, d);
-      loadv<T, VEC>(vv + r * a.h, v);
-      const float2 st = *reinterpret_cast<const float2*>(a.stats + 2 * r);
+    for (long r0 = rg; r0 < a.rows; r0 += (long)U * RG) {
+      uint4 pd[U], pv[U];
+      float2 st[U];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        ag[e] += d[e] * ((v[e] - st.x) * st.y);
-        ab[e] += d[e];
+      for (int u = 0; u < U; ++u) {
+        const long r = r0 + (long)u * RG;
+        if (r < a.rows) {
+          pd[u] = *reinterpret_cast<const uint4*>(dy + r * a.h);
+          pv[u] = *reinterpret_cast<const uint4*>(vv + r * a.h);
+          st[u] = *reinterpret_cast<const float2*>(a.stats + 2 * r);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (r0 + (long)u * RG < a.rows) {
+          float d[VEC], v[VEC];
+          ln::unpack<T>(pd[u], d);
+          ln::unpack<T>(pv[u], v);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            ag[e] += d[e] * ((v[e] - st[u].x) * st[u].y);
+            ab[e] += d[e];
+          }
+        }
       }
     }
   }

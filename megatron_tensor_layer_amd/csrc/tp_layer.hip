@@ -938,6 +938,7 @@ hipError_t ln_fwd_launch(const LnFwdArgs& a, hipStream_t st) {
   } else {
     const unsigned g = (unsigned)a.rows;
     if (nch <= 256 * 4) hipLaunchKernelGGL((ln_fwd_kernel<T, 256, 4>), dim3(g), dim3(256), 0, st, a);
+    else if (nch <= 256 * 6) hipLaunchKernelGGL((ln_fwd_kernel<T, 256, 6>), dim3(g), dim3(256), 0, st, a);
     else if (nch <= 256 * 8) hipLaunchKernelGGL((ln_fwd_kernel<T, 256, 8>), dim3(g), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((ln_fwd_kernel<T, 256, 16>), dim3(g), dim3(256), 0, st, a);
   }
@@ -960,6 +961,7 @@ hipError_t ln_bwd_launch(const LnBwdArgs& a, hipStream_t st) {
     } else {
       const unsigned g = (unsigned)a.rows;
       if (nch <= 256 * 4) hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 256, 4>), dim3(g), dim3(256), 0, st, a);
+      else if (nch <= 256 * 6) hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 256, 6>), dim3(g), dim3(256), 0, st, a);
       else if (nch <= 256 * 8) hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 256, 8>), dim3(g), dim3(256), 0, st, a);
       else hipLaunchKernelGGL((ln_bwd_dx_kernel<T, 256, 16>), dim3(g), dim3(256), 0, st, a);
     }

@@ -31,7 +31,7 @@ def _need_gpu(gpu):
 
 LN_CASES = [
     ("fp32", 5, 64), ("fp32", 33, 2048 + 8), ("fp32", 7, 16384),
-    ("bf16", 1, 8), ("bf16", 9, 4096), ("bf16", 6, 4104), ("bf16", 5, 8192 + 64), ("bf16", 3, 32768),
+    ("bf16", 1, 8), ("bf16", 9, 4096), ("bf16", 6, 4104), ("bf16", 5, 8192 + 64), ("bf16", 4, 12288 + 8), ("bf16", 3, 32768),
     ("bf16", 256, 12288),   # 175B: 2048 tokens / 8 ranks
     ("bf16", 512, 6144),    # 18B: 4096 tokens / 8 ranks
     ("bf16", 256, 25600),   # 1T
