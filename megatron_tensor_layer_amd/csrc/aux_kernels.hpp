@@ -161,15 +161,15 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const T* __restrict__ dC, c
 // ---------------------------------------------------------------------------
 // out[n] = sum_r X[r, n]: bias gradients in one fixed-order pass. A block owns
 // 8 x VEC columns (8 column threads of 16 bytes: a 128-byte row piece) over all
-// R rows. Its 32 row groups each sum rows rg, rg + 32, ... with 16 loads in
-// flight per thread (64 KB per block, enough to cover HBM latency with one
-// block per CU), then a fixed LDS tree adds the groups and the result is
-// rounded once.
+// R rows. Its NT/8 row groups each sum rows rg, rg + NT/8, ... with 16 loads in
+// flight per thread (64 KB per 256-thread block, enough to cover HBM latency
+// with one block per CU), then a fixed LDS tree adds the groups and the result
+// is rounded once.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(256) colsum_kernel(const T* __restrict__ X, T* __restrict__ out, int R, int N,
-                                                     long ld) {
-  constexpr int VEC = Elt<T>::VEC, CT = 8, RG = 256 / CT, W = CT * VEC, U = 16;
+template <typename T, int NT>
+__global__ void __launch_bounds__(NT) colsum_kernel(const T* __restrict__ X, T* __restrict__ out, int R, int N,
+                                                    long ld) {
+  constexpr int VEC = Elt<T>::VEC, CT = 8, RG = NT / CT, W = CT * VEC, U = 16;
   const int ct = threadIdx.x % CT, rg = threadIdx.x / CT;
   const int col = (blockIdx.x * CT + ct) * VEC;
   float acc[VEC];
@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(256) colsum_kernel(const T* __restrict__ X, T*
   for (int e = 0; e < VEC; ++e) red[rg][ct * VEC + e] = acc[e];
   __syncthreads();
   for (int h = RG / 2; h >= 1; h /= 2) {  // fixed tree over the row groups
-    for (int i = threadIdx.x; i < h * W; i += 256) red[i / W][i % W] += red[i / W + h][i % W];
+    for (int i = threadIdx.x; i < h * W; i += NT) red[i / W][i % W] += red[i / W + h][i % W];
     __syncthreads();
   }
   if (threadIdx.x < W) {

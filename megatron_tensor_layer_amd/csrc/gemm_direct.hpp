@@ -93,6 +93,7 @@ struct DirectOperand {
   static_assert(INSTS % WAVES == 0, "tile must split evenly over the waves");
   static constexpr int PER_WAVE = INSTS / WAVES;
   static constexpr int ROW_UNITS = R / 8;  // 16-byte units per k-row (M/N-major)
+  static_assert(KMAJ || 64 % ROW_UNITS == 0, "an M/N-major load instruction covers whole k-rows of the tile");
   uint32_t off[PER_WAVE];                  // element offsets at the tile's k origin
 
   __device__ __forceinline__ void init(long ld, int mn0, int lim, int wave, int lane) {

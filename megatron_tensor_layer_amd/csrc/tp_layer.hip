@@ -29,6 +29,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <map>
 #include <cmath>
 #include <mutex>
 #include <type_traits>
@@ -161,6 +162,7 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 #define TPL_BIG_WN 2
 #endif
 using CfgBig = TileCfg<bf16_t, 256, 256, 2, TPL_BIG_WN>;  // linear GEMMs
+using CfgB192 = TileCfg<bf16_t, 192, 256, 2, TPL_BIG_WN>;  // linear GEMMs of one partial wave
 using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
 using CfgF32 = TileCfg<float, 64, 64, 2, 2>;     // fp32 configuration
 
@@ -293,30 +295,69 @@ size_t partial_bytes(const Dims& D, long M, long N, long K) {
 }
 
 // Grouped launch of two GEMMs (M0 x N0 x K0 first, M1 x N1 x K1 second):
-// problem 0 is split along K when its tiles run far longer than the average
-// work per CU, so that the split pieces and problem 1's tiles fill the
-// 256 CUs together. Returns the split count and its chunk (a multiple of BK).
+// problem 0 may be split along K so that its pieces and problem 1's tiles
+// fill the 256 CUs together. The dispatcher hands the blocks out in order
+// (the problem with the longer units first) to whichever CU frees first; the
+// plan simulates exactly that for each split count and takes the fastest,
+// counting a per-unit epilogue cost and, for a split, the HBM traffic of the
+// fp32 partials (written by the pieces, read back by the reduction, which
+// also writes the result). Returns the split count and its chunk (a multiple
+// of BK).
 struct PairPlan {
   int splits;
   long chunk;
 };
-PairPlan pair_plan(long M0, long N0, long K0, long M1, long N1, long K1) {
+
+// Finish time of handing n1 units of length l1, then n2 of length l2, in
+// order, each to whichever of the 256 CUs frees first. CUs free at the same
+// time are kept as one bucket, so a step places a whole batch of units.
+double dispatch_makespan(long n1, double l1, long n2, double l2) {
+  std::map<double, long> free_at{{0.0, 256}};
+  auto place = [&](long n, double len) {
+    while (n > 0) {
+      auto it = free_at.begin();
+      const double t = it->first;
+      const long k = std::min(it->second, n);
+      if (k == it->second) free_at.erase(it);
+      else it->second -= k;
+      free_at[t + len] += k;
+      n -= k;
+    }
+  };
+  place(n1, l1);
+  place(n2, l2);
+  return free_at.rbegin()->first;
+}
+
+PairPlan pair_plan(long M0, long N0, long K0, long M1, long N1, long K1, bool gelu0 = false) {
   const long t0 = cdivl(M0, CfgBig::BM) * cdivl(N0, CfgBig::BN);
   const long t1 = cdivl(M1, CfgBig::BM) * cdivl(N1, CfgBig::BN);
   const long it0 = cdivl(K0, CfgBig::BK), it1 = cdivl(K1, CfgBig::BK);
-  const double per_cu = ((double)t0 * it0 + (double)t1 * it1) / 256.0;
-  PairPlan P{1, K0};
-  if (it0 > 1.5 * per_cu && it0 >= 32) {
-    long sp = std::min<long>((long)std::ceil(it0 / per_cu), it0 / 16);
+  const double t_it = 1.6e-6;                   // one K step of a 256 x 256 tile, all CUs busy
+  const double epi = 2.0, epi_part = 3.0;       // epilogue in K steps: bf16 tile, fp32 partial tile
+  PairPlan best{1, K0};
+  double best_t = 0.0, whole_t = 0.0;
+  const long max_sp = K0 % CfgBig::BK == 0 ? std::min<long>(16, it0 / 8) : 1;
+  for (long sp = 1; sp <= std::max<long>(1, max_sp); ++sp) {
     const long chunk = cdivl(it0, sp);
-    P.splits = (int)cdivl(it0, chunk);
-    P.chunk = chunk * CfgBig::BK;
+    if (cdivl(it0, chunk) != sp) continue;  // the same split as a smaller count
+    const double l0 = (double)chunk + (sp > 1 ? epi_part : epi), l1 = (double)it1 + epi;
+    const double span = l0 >= l1 ? dispatch_makespan(t0 * sp, l0, t1, l1) : dispatch_makespan(t1, l1, t0 * sp, l0);
+    double t = span * t_it;
+    if (sp > 1) t += (double)M0 * N0 * (8.0 * sp + 2.0 + (gelu0 ? 2.0 : 0.0)) / 4.5e12 + 4e-6;  // partials
+    if (sp == 1) whole_t = best_t = t;
+    // a split must win clearly: its partials also evict cached operands that
+    // the kernels after it would read again
+    else if (t < best_t && t < 0.97 * whole_t) {
+      best_t = t;
+      best = PairPlan{(int)sp, chunk * CfgBig::BK};
+    }
   }
-  return P;
+  return best;
 }
-size_t pair_partial_bytes(const Dims& D, long M0, long N0, long K0, long M1, long N1, long K1) {
+size_t pair_partial_bytes(const Dims& D, long M0, long N0, long K0, long M1, long N1, long K1, bool gelu0) {
   if (D.dt != TP_BF16) return 0;
-  const PairPlan P = pair_plan(M0, N0, K0, M1, N1, K1);
+  const PairPlan P = pair_plan(M0, N0, K0, M1, N1, K1, gelu0);
   return P.splits > 1 ? al((size_t)P.splits * M0 * N0 * 4) : 0;
 }
 
@@ -332,17 +373,17 @@ WsLayout ws_layout(const Dims& D, int blk) {
   size_t pb = 0;
   auto upd = [&](long M, long N, long K) { pb = std::max(pb, partial_bytes(D, M, N, K)); };
   // input- and weight-gradient GEMMs of one weight, grouped
-  auto upd2 = [&](long M0, long N0, long K0, long M1, long N1, long K1) {
+  auto upd2 = [&](long M0, long N0, long K0, long M1, long N1, long K1, bool gelu0) {
     upd(M0, N0, K0);
     upd(M1, N1, K1);
-    pb = std::max(pb, pair_partial_bytes(D, M0, N0, K0, M1, N1, K1));
+    pb = std::max(pb, pair_partial_bytes(D, M0, N0, K0, M1, N1, K1, gelu0));
   };
   // the flash attention chunks share the partials region (every user runs in
   // turn on the stream)
   if (flash(D)) pb = std::max(pb, al(fa_part_bytes(D, blk)));
   if (blk == TP_ATTN) {
     upd(D.T, D.q3, D.h); upd(D.T, D.h, D.hr);
-    upd2(D.T, D.hr, D.h, D.hr, D.h, D.T); upd2(D.T, D.h, D.q3, D.h, D.q3, D.T);
+    upd2(D.T, D.hr, D.h, D.hr, D.h, D.T, false); upd2(D.T, D.h, D.q3, D.h, D.q3, D.T, false);
     const bool fl = flash(D);
     size_t fwd = fl ? 0 : al((size_t)D.z * D.s * D.s * 4);
     W.qkv_lo = fwd;
@@ -356,7 +397,7 @@ WsLayout ws_layout(const Dims& D, int blk) {
     W.part = std::max(fwd, o);
   } else {
     upd(D.T, D.fr, D.h); upd(D.T, D.h, D.fr);
-    upd2(D.T, D.fr, D.h, D.fr, D.h, D.T); upd2(D.T, D.h, D.fr, D.h, D.fr, D.T);
+    upd2(D.T, D.fr, D.h, D.fr, D.h, D.T, true); upd2(D.T, D.h, D.fr, D.h, D.fr, D.T, false);
     W.du = 0;
     W.part = al((size_t)D.T * D.fr * D.es);
   }
@@ -471,6 +512,16 @@ GemmArgs gargs(long M, long N, long K) {
     if (e_ != hipSuccess) return e_; \
   } while (0)
 
+// A launch of whole 256 x 256 tiles that leaves CUs idle (fewer tiles than
+// CUs) spreads the same work over more CUs with 192-row tiles when those
+// still fit one wave: 175B QKV 144 -> 198 tiles. The shorter tile does 3/4
+// of the work at about 0.82 of the 256-row tile's rate, so this pays when
+// it adds more than a few tiles.
+bool tall_tiles_pay(const GemmArgs& p) {
+  const long t256 = cdivl(p.M, 256) * cdivl(p.N, 256), t192 = cdivl(p.M, 192) * cdivl(p.N, 256);
+  return direct_ok<CfgB192>(p, 1) && t256 < 256 && t192 <= 256 && (double)t192 >= 1.15 * (double)t256;
+}
+
 // Linear (weight) GEMM M x N x K: split-K chosen for the bf16 path.
 template <bool AK, bool BKM, int EPI, int ROLE>
 hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
@@ -494,6 +545,11 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
     }
     p.splits = choose_splits(p.M, p.N, p.K);
     p.part = part;
+    // (the M-contiguous A loader is laid out for 256-row tiles only)
+    if constexpr (AK && (ROLE == R_QKV_FWD || ROLE == R_O_FWD || ROLE == R_FC1_FWD || ROLE == R_FC2_FWD ||
+                         ROLE == R_GEMM)) {
+      if (p.splits == 1 && tall_tiles_pay(p)) return launch<CfgB192, AK, BKM, EPI, bf16_t, ROLE>(p, 1, st);
+    }
   }
   return run<AK, BKM, EPI, ROLE, KIND_BIG>(D, p, 1, st);
 }
@@ -523,7 +579,7 @@ hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_
     q->splits = 1;
   }
   const int tiles0 = p0.tiles_m * p0.tiles_n, tiles1 = p1.tiles_m * p1.tiles_n;
-  const PairPlan P = pair_plan(p0.M, p0.N, p0.K, p1.M, p1.N, p1.K);
+  const PairPlan P = pair_plan(p0.M, p0.N, p0.K, p1.M, p1.N, p1.K, E0 == EPI_GELU_BWD);
   const int splits = P.splits;
   if (splits > 1) {
     p0.splits = splits;
@@ -546,15 +602,19 @@ hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_
 }
 
 // Column sums (bias gradients), one fixed-order pass.
+#ifndef TPL_COLSUM_NT
+#define TPL_COLSUM_NT 256
+#endif
+
 template <int ROLE>
 hipError_t colsum(const Dims& D, const void* X, void* out, long R, long N, long ld, hipStream_t st) {
   prof::Scope sc(ROLE, (double)R * N, (double)D.es * (R * N + N), st);
   if (D.dt == TP_BF16)
-    hipLaunchKernelGGL(colsum_kernel<bf16_t>, dim3((unsigned)cdivl(N, 64)), dim3(256), 0, st, (const bf16_t*)X,
-                       (bf16_t*)out, (int)R, (int)N, ld);
+    hipLaunchKernelGGL((colsum_kernel<bf16_t, TPL_COLSUM_NT>), dim3((unsigned)cdivl(N, 64)), dim3(TPL_COLSUM_NT), 0,
+                       st, (const bf16_t*)X, (bf16_t*)out, (int)R, (int)N, ld);
   else
-    hipLaunchKernelGGL(colsum_kernel<float>, dim3((unsigned)cdivl(N, 32)), dim3(256), 0, st, (const float*)X,
-                       (float*)out, (int)R, (int)N, ld);
+    hipLaunchKernelGGL((colsum_kernel<float, TPL_COLSUM_NT>), dim3((unsigned)cdivl(N, 32)), dim3(TPL_COLSUM_NT), 0,
+                       st, (const float*)X, (float*)out, (int)R, (int)N, ld);
   return hipGetLastError();
 }
 

@@ -58,7 +58,11 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
 # reference from the same bf16 operands; a second call must match bitwise.
 @pytest.mark.parametrize("M,N,K,ak,bk,plan", [
     (2064, 4624, 12288, 1, 0, "sk"),   # 171 tiles < one wave: all stream-K (c = 129 of 192 iterations)
-    (2064, 4112, 12288, 1, 1, "dp"),   # 153 tiles: one partial wave of whole tiles
+    (2064, 4112, 12288, 1, 1, "dp192"),  # 153 tiles of 256 rows: one partial wave of 187 192-row tiles
+    (2048, 4608, 12288, 1, 0, "dp192"),  # the 175B QKV shape: 144 -> 198 tiles (3 passes of 64 staged rows)
+    (1936, 4112, 12288, 1, 1, "dp192"),  # ragged M in 192-row tiles (1936 = 10 x 192 + 16)
+    (1936, 4112, 12288, 0, 1, "dp"),     # M-contiguous A: 256-row tiles only
+    (2048, 6144, 2048, 1, 1, "dp"),    # 192 tiles, one partial wave: 256 more 192-row tiles would not fit
     (2064, 8208, 6144, 0, 0, "sk"),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
     (2064, 8208, 6144, 0, 1, "sk"),
     (1040, 2832, 4096, 1, 0, "split"),  # 60 tiles: split-K
@@ -74,7 +78,7 @@ def test_gemm_launch_plans_full_size(M, N, K, ak, bk, plan):
     Bd = torch.from_numpy(np.ascontiguousarray(B.T) if bk else B).to("cuda", bf)
     bd = torch.from_numpy(bias).to("cuda", bf)
     # stream-K and split-K keep fp32 partials in the workspace; whole tiles need none
-    assert (tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K) > 0) == (plan != "dp")
+    assert (tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K) > 0) == (not plan.startswith("dp"))
     outs = []
     for _ in range(2):
         C = torch.full((M, N), float("nan"), device="cuda", dtype=bf)
