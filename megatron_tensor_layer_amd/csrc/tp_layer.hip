@@ -163,6 +163,7 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 #endif
 using CfgBig = TileCfg<bf16_t, 256, 256, 2, TPL_BIG_WN>;  // linear GEMMs
 using CfgB192 = TileCfg<bf16_t, 192, 256, 2, TPL_BIG_WN>;  // linear GEMMs of one partial wave
+using CfgHalf = TileCfg<bf16_t, 256, 128, 2, 2>;              // the columns past whole waves
 using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
 using CfgF32 = TileCfg<float, 64, 64, 2, 2>;     // fp32 configuration
 
@@ -522,6 +523,21 @@ bool tall_tiles_pay(const GemmArgs& p) {
   return direct_ok<CfgB192>(p, 1) && t256 < 256 && t192 <= 256 && (double)t192 >= 1.15 * (double)t256;
 }
 
+// Columns of a whole-tile launch that fill whole waves of 256 CUs with
+// 256 x 256 tiles when the other tiles (at most half a wave) would run as a
+// partial wave. Those remaining columns then run as 256 x 128 tiles, twice as
+// many, which still fit one wave and take about half as long: 175B O
+// projection, 384 tiles = 1.5 waves -> 256 tiles, then 256 half tiles.
+// 0 when the split does not apply.
+long whole_wave_cols(const GemmArgs& p) {
+  const long tm = cdivl(p.M, 256), tn = cdivl(p.N, 256), tiles = tm * tn;
+  const long W = tiles / 256, R = tiles % 256;
+  if (W < 1 || R == 0 || R > 128 || (256 * W) % tm != 0) return 0;
+  const long n1 = 256 * (256 * W / tm);
+  if (n1 >= p.N || (p.N - n1) % 8 != 0) return 0;
+  return n1;
+}
+
 // Linear (weight) GEMM M x N x K: split-K chosen for the bf16 path.
 template <bool AK, bool BKM, int EPI, int ROLE>
 hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
@@ -549,6 +565,20 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
     if constexpr (AK && (ROLE == R_QKV_FWD || ROLE == R_O_FWD || ROLE == R_FC1_FWD || ROLE == R_FC2_FWD ||
                          ROLE == R_GEMM)) {
       if (p.splits == 1 && tall_tiles_pay(p)) return launch<CfgB192, AK, BKM, EPI, bf16_t, ROLE>(p, 1, st);
+    }
+    if constexpr (EPI == EPI_LINEAR && (ROLE == R_O_FWD || ROLE == R_FC2_FWD || ROLE == R_GEMM)) {
+      const long n1 = (p.splits == 1 && !p.resid && direct_ok<CfgBig>(p, 1)) ? whole_wave_cols(p) : 0;
+      if (n1 > 0) {
+        GemmArgs a = p;
+        a.N = (int)n1;
+        TRY_E((launch<CfgBig, AK, BKM, EPI, bf16_t, ROLE>(a, 1, st)));
+        GemmArgs b = p;
+        b.N = p.N - (int)n1;
+        b.B = static_cast<const bf16_t*>(p.B) + (BKM ? n1 * p.ldb : n1);
+        b.C = static_cast<bf16_t*>(p.C) + n1;
+        if (p.bias) b.bias = static_cast<const bf16_t*>(p.bias) + n1;
+        return launch<CfgHalf, AK, BKM, EPI, bf16_t, ROLE>(b, 1, st);
+      }
     }
   }
   return run<AK, BKM, EPI, ROLE, KIND_BIG>(D, p, 1, st);
