@@ -471,7 +471,11 @@ def main():
                    "parallelism": f"tp{t} ranks run sequentially on one GPU"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "rank_ms": round(t_rank, 4),
+        "rank_ms_median": round(float(np.median(rank_loops)) / t, 4),
         "rank_ms_min": round(float(np.min(rank_loops)) / t, 4),
+        "peak_used": {"tflops": PEAK_BF16_TFLOPS, "cus": 256, "clock_ghz": 2.4, "flop_per_clk_per_cu": 4096,
+                      "cus_on_device": int(torch.cuda.get_device_properties(0).multi_processor_count),
+                      "device": torch.cuda.get_device_properties(0).name},
         "standin_reduce_ms_per_step": round(float(np.mean(standin)), 4),
         "flops_per_rank": F_rank,
         "wall_s_timed": round(wall, 3),
