@@ -256,33 +256,36 @@ def test_recompute_with_sequence_parallelism():
         assert torch.equal(getattr(a_, attr), getattr(b_, attr)), attr
 
 
-def test_recompute_full_size_rank0_mlp_matches_saved_path():
-    """175B shard, rank 0's MLP block at its real shape, in the launch
+@pytest.mark.parametrize("blk", ["attn", "mlp"])
+def test_recompute_full_size_rank0_matches_saved_path(blk):
+    """175B shard, rank 0's block at its real shape, in the launch
     configuration the benchmark times: the recomputing backward gives the
     saved path's gradients bit for bit (the saved path is checked against the
     oracle at this size by the hot-path tests)."""
     cfg = I.CONFIGS["gpt_175b"]
     h, a, s, b, t = cfg.h, cfg.a, cfg.s, cfg.b, cfg.t
+    block = tp.TP_ATTN if blk == "attn" else tp.TP_MLP
+    print(f"recompute full size {blk}", flush=True)
     dt = tp.TP_BF16
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(7)
+    gen.manual_seed(8)
     rnd = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device="cuda") * std).to(torch.bfloat16)  # noqa
-    w = tuple(rnd(*shp, std=0.02) for shp in tp.block_shapes(h, t, tp.TP_MLP))
+    w = tuple(rnd(*shp, std=0.02) for shp in tp.block_shapes(h, t, block))
     x, dy = rnd(s * b, h), rnd(s * b, h)
-    saved = torch.empty(tp.tp_saved_bytes(h, a, s, b, t, dt, tp.TP_MLP), dtype=torch.uint8, device="cuda")
-    ws = torch.empty(tp.tp_workspace_bytes(h, a, s, b, t, dt, tp.TP_MLP), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(tp.tp_saved_bytes(h, a, s, b, t, dt, block), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tp.tp_workspace_bytes(h, a, s, b, t, dt, block), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
     outs = []
     for rec in (False, True):
         grads = tuple(torch.full(shp, float("nan"), dtype=torch.bfloat16, device="cuda")
-                      for shp in tp.block_shapes(h, t, tp.TP_MLP))
+                      for shp in tp.block_shapes(h, t, block))
         dx = torch.full_like(x, float("nan"))
         if rec:
             scratch = torch.full_like(saved, 0xFF)   # the recompute must not read stale contents
-            tp.tp_layer_bwd_recompute(h, a, s, b, t, 0, dt, tp.TP_MLP, x, w, dy, dx, grads, scratch, ws)
+            tp.tp_layer_bwd_recompute(h, a, s, b, t, 0, dt, block, x, w, dy, dx, grads, scratch, ws)
         else:
-            tp.tp_layer_fwd(h, a, s, b, t, 0, dt, tp.TP_MLP, x, w, y, saved, ws)
-            tp.tp_layer_bwd(h, a, s, b, t, 0, dt, tp.TP_MLP, x, w, saved, dy, dx, grads, ws)
+            tp.tp_layer_fwd(h, a, s, b, t, 0, dt, block, x, w, y, saved, ws)
+            tp.tp_layer_bwd(h, a, s, b, t, 0, dt, block, x, w, saved, dy, dx, grads, ws)
         torch.cuda.synchronize()
         outs.append((dx, grads))
     assert torch.equal(outs[0][0], outs[1][0])
