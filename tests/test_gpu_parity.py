@@ -65,6 +65,8 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
     (2048, 6144, 2048, 1, 1, "dp"),    # 192 tiles, one partial wave: 256 more 192-row tiles would not fit
     (2048, 12288, 1536, 1, 0, "dp+half"),  # the 175B O projection: 256 tiles, then 8192.. as 256 x 128 tiles
     (2048, 10256, 1536, 1, 1, "dp+half"),  # 328 tiles: 8192 columns whole, 2064 (ragged) in 136 half tiles
+    (2048, 12288, 1536, 0, 0, "dp+half"),  # M-contiguous A and N-contiguous B in the half tiles
+    (2048, 10256, 1536, 0, 1, "dp+half"),
     (2064, 8208, 6144, 0, 0, "sk"),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
     (2064, 8208, 6144, 0, 1, "sk"),
     (1040, 2832, 4096, 1, 0, "split"),  # 60 tiles: split-K
