@@ -171,8 +171,10 @@ int tp_layer_bwd_recompute(int h, int a, int s, int b, int t, int rank, int dtyp
  * is required); otherwise beta, y and stats are required.
  *   x, residual, sum_out, y  [rows, h];  bias, gamma, beta [h]
  * h must be a multiple of 8 and at most 32768 (bf16) or 16384 (fp32)
- * (TP_EUNSUPPORTED); eps >= 0. stats needs 8-byte alignment, every other
- * pointer 16. y and sum_out must not alias the inputs of another row. The page does not write LayerNorm out: this is the textbook
+ * (TP_EUNSUPPORTED); eps >= 0 and finite (TP_EINVAL). stats needs 8-byte
+ * alignment, every other pointer 16 (TP_EALIGN). y and sum_out must not
+ * alias the inputs of another row. rows == 0: TP_OK, nothing is read or
+ * written. The page does not write LayerNorm out: this is the textbook
  * definition.                                                                */
 int tp_layernorm_fwd(int dtype, long rows, long h, float eps, const void *x, const void *bias,
                      const void *residual, const void *gamma, const void *beta, void *sum_out, void *y,
@@ -189,7 +191,9 @@ int tp_layernorm_fwd(int dtype, long rows, long h, float eps, const void *x, con
  * With sequence parallelism the rows are the rank's own tokens, so dgamma
  * and dbeta are this rank's partial sums: their sum over the ranks (the
  * all-reduce of the replicated LayerNorm weights' gradients) is the full
- * gradient. dx must not alias dy or v.                                       */
+ * gradient. dx must not alias dy or v. Sizes, alignment and errors as
+ * tp_layernorm_fwd; rows == 0 writes zeros to dgamma and dbeta (if given)
+ * and reads nothing else.                                                    */
 int tp_layernorm_bwd(int dtype, long rows, long h, const void *dy, const void *v, const float *stats,
                      const void *gamma, const void *dresid, void *dx, void *dgamma, void *dbeta, void *stream);
 
