@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module", autouse=True)
 def _need_gpu(gpu):
-    tp.lib()  # fail loudly if the library is missing on a GPU machine
+    tp.lib()  # fail loudly if the library is missing where a GPU is present
     yield
 
 
