@@ -666,15 +666,26 @@ fa_bwd_dkv_kernel(const FaArgs a) {
       fa::zero(st[1]);
       fa::split_scores<KS>(Lq, Lq + TL::U4, lo, kh, kl, st);
       // P^T (keys x queries), visible iff key <= query < s
-      const bool edge = fa::BT * t < kmin + 32 || fa::BT * t + fa::BT > a.s;
+      // (tiles clear of the diagonal and the sequence end take a branch-free
+      // loop; a per-element mask would become one branch per element)
+      if (fa::BT * t < kmin + 32 || fa::BT * t + fa::BT > a.s) {
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int c = fa::acc_col(bb, e, g), q = fa::BT * t + c;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][e], a.sl2, -Lf[c]));
-          st[bb][e] = (edge && (q < krow || q >= a.s)) ? 0.0f : p;
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int c = fa::acc_col(bb, e, g), q = fa::BT * t + c;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][e], a.sl2, -Lf[c]));
+            st[bb][e] = (q < krow || q >= a.s) ? 0.0f : p;
+          }
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int c = fa::acc_col(bb, e, g);
+            st[bb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][e], a.sl2, -Lf[c]));
+          }
+      }
       fa::tr_products<NB>(Ld, lo, st, dv);  // dV += P^T dC
       // dP^T = V dC^T;  dS^T = P^T (dP^T - D) / sqrt(d)
       f32x16_t dp[2];
