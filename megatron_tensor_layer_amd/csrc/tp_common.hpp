@@ -71,12 +71,32 @@ template <> struct Elt<bf16_t> {
   __device__ static __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
 };
 
-// Exact (erf-form) GELU and its derivative in fp32.
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// GELU(x) = x Phi(x) (erf form) and GELU'(x) = Phi(x) + x phi(x) in fp32,
+// branch-free. Phi from the rational approximation of erfc in Abramowitz &
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26 (|error| of erf
+// <= 1.5e-7): with z = |x|/sqrt(2) and t = 1/(1 + p z),
+// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), and
+// exp(-z^2) = exp(-x^2/2) is also phi(x) sqrt(2 pi). The small tail Phi(-|x|)
+// is formed directly, without the cancellation of 1 + erf(x/sqrt(2)).
+// (An erff call branches on |x| per element.)
+struct NormalCdf {
+  float cdf, e;  // Phi(x) and exp(-x^2/2)
+};
+__device__ __forceinline__ NormalCdf normal_cdf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
+  float q = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+  q = __builtin_fmaf(t, q, 1.421413741f);
+  q = __builtin_fmaf(t, q, -0.284496736f);
+  q = __builtin_fmaf(t, q, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x);  // exp(-x^2/2) = 2^(-x^2 log2(e)/2)
+  const float tail = 0.5f * t * q * e;                                     // Phi(-|x|)
+  return {x >= 0.0f ? 1.0f - tail : tail, e};
+}
+__device__ __forceinline__ float gelu_f(float x) { return x * normal_cdf(x).cdf; }
 __device__ __forceinline__ float gelu_grad_f(float x) {
-  const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
-  const float pdf = 0.39894228040143268f * expf(-0.5f * x * x);
-  return cdf + x * pdf;
+  const NormalCdf n = normal_cdf(x);
+  return __builtin_fmaf(x * 0.39894228040143268f, n.e, n.cdf);
 }
 
 // V consecutive elements (V = 4 or 8) as fp32.
