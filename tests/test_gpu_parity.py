@@ -341,3 +341,46 @@ def test_profiler_attributes_every_role(name):
     assert prof["reduce"]["launches"] == 4
     T, h, t = cfg.tokens, cfg.h, cfg.t
     assert prof["fc1_fwd"]["flops"] == pytest.approx(t * 2.0 * T * (4 * h // t) * h)
+
+
+# ---------------------------------------------------------------------------
+# GELU and GELU' epilogues, element by element over a wide input range
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_gelu_epilogues_element_by_element(dtype):
+    """Rank 1 of an MLP block whose FC1 weight is zero, so U = b1, and whose
+    FC2 weight shard is a partial identity, so the block output holds
+    Z = GELU(b1) column by column; with dY = 1/T in every row the FC1 bias
+    gradient is sum_tokens dU = GELU'(b1) (a power-of-two scale commutes with
+    rounding). b1 spans [-8, 8], tails included. Reference: the oracle's exact
+    (erf-form) GELU and GELU' on the same (rounded) b1."""
+    from megatron_tensor_layer_amd.layer import TPLayer
+    h, a, s, b, t = 256, 2, 64, 2, 2
+    T, fr = s * b, 4 * h // t
+    code = tp.TP_BF16 if dtype == "bf16" else tp.TP_FP32
+    dt = tp.torch_dtype(code)
+    b1 = torch.zeros(fr, dtype=dt, device="cuda")
+    b1[:h] = torch.linspace(-8.0, 8.0, h, device="cuda")
+    w2 = torch.zeros((fr, h), dtype=dt, device="cuda")
+    w2[torch.arange(h), torch.arange(h)] = 1.0
+    mlp = (torch.zeros((h, fr), dtype=dt, device="cuda"), b1, w2, torch.zeros(h, dtype=dt, device="cuda"))
+    attn = tuple(torch.zeros(shp, dtype=dt, device="cuda") for shp in tp.block_shapes(h, t, tp.TP_ATTN))
+    layer = TPLayer(h, a, s, b, t, code, [{"attn": attn, "mlp": mlp} for _ in range(t)])
+    x = torch.randn((T, h), device="cuda").to(dt)
+    out = torch.empty((T, h), dtype=dt, device="cuda")
+    layer.block_fwd(tp.TP_MLP, 1, x, out)
+    dy = torch.full((T, h), 1.0 / T, dtype=dt, device="cuda")
+    dx = torch.empty_like(out)
+    layer.block_bwd(tp.TP_MLP, 1, x, dy, dx)
+    torch.cuda.synchronize()
+    u = to_np(b1[:h])
+    # the device's Phi is within 3e-7 of the exact one (times |x| <= 8 in GELU);
+    # bf16 adds one rounding of the output (2^-8 relative); fp32 adds the fixed-
+    # order fp32 sum of the 128 token rows in the bias gradient
+    rel, floor = (2.0 ** -8, 4e-7 * 8) if dtype == "bf16" else (1e-5, 4e-7 * 8)
+    z = to_np(out)
+    ref_z = O.gelu(u)
+    assert np.all(np.abs(z - ref_z[None, :]) <= rel * np.abs(ref_z)[None, :] + floor), "GELU"
+    g = to_np(layer.grads[1]["mlp"][1][:h])
+    ref_g = O.gelu_grad(u)
+    assert np.all(np.abs(g - ref_g) <= rel * np.abs(ref_g) + floor), "GELU'"
