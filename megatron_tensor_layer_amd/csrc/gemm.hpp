@@ -62,7 +62,11 @@ struct GemmArgs {
   int kmode;
   int splits, k_chunk;   // split-K (EPI_PARTIAL pass)
   int group_m;           // tile-rows per ordering group
-  int no_xcd;            // 1: tile index is used as given (the launch maps blocks to XCDs itself)
+  int no_xcd;            // 1: tile index is used as given (the launch maps blocks to XCDs itself);
+                         // 2: as 1, and stream-K tiles (index >= skm_base) are placed by the skm_* map
+  int skm_base, skm_col0;  // first stream-K tile index; first tile-column of the stream-K region
+  int skm_br, skm_bc;      // tiles of one XCD: a block of skm_br x skm_bc tiles
+  int skm_q, skm_gr, skm_gc;  // runs of one K phase: skm_q groups of skm_gr x skm_gc tiles per block
   int kseg, kseg_len;    // kseg = 3: K runs over (A,B), (A,B2), (A2,B), each kseg_len long
   int c2_cols;           // EPI_BIAS_SPLIT: columns that get a residual in C2
   const void* A; long lda, a_s1, a_s2;
@@ -371,6 +375,20 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn,
     while (m * (m + 1) / 2 > L) --m;
     tm = m;
     tn = L - m * (m + 1) / 2;
+    return;
+  }
+  if (p.no_xcd == 2 && L >= p.skm_base) {
+    // stream-K tile j: XCD x's runs cover tiles [x n, (x + 1) n), n = br bc,
+    // placed as one br x bc block; tile i = q k + d of the block belongs to
+    // K-phase group d (the runs that work at the same K offset at the same
+    // time), placed as a gr x gc sub-block, so concurrent runs share operand
+    // panels in the XCD's L2
+    const int j = L - p.skm_base, n = p.skm_br * p.skm_bc;
+    const int x = j / n, i = j - (j / n) * n;
+    const int k = i / p.skm_q, d = i - (i / p.skm_q) * p.skm_q;
+    const int gpr = p.skm_bc / p.skm_gc, bpr = p.tiles_m / p.skm_br;
+    tm = (x % bpr) * p.skm_br + (d / gpr) * p.skm_gr + k % p.skm_gr;
+    tn = p.skm_col0 + (x / bpr) * p.skm_bc + (d % gpr) * p.skm_gc + k / p.skm_gr;
     return;
   }
   const int tiles = p.tiles_m * p.tiles_n;

@@ -286,6 +286,39 @@ SkPlan sk_plan(long M, long N, long K) {
 }
 
 
+// Placement of a stream-K region's tiles (GemmArgs skm_*; no_xcd = 2) when
+// every XCD's 32 runs cover whole tiles and the region is whole tile-columns
+// of at most 8 tile-rows (one ordering group, so the whole tiles before it
+// are the columns before it): the XCD's tiles as one compact block, and the
+// tiles its runs work on at the same K offset (a period of q tiles) as
+// compact sub-blocks. 175B FC1 forward: 2 x 12 blocks, 3 groups of 2 x 4.
+void sk_place(GemmArgs& p, const SkPlan& s) {
+  const long per = (long)(s.units / 8) * s.c;
+  if (s.units % 8 || per % s.iters || p.tiles_m > 8 || s.sk_tiles % p.tiles_m || s.dp_tiles % p.tiles_m) return;
+  const int n = (int)(per / s.iters), cols = s.sk_tiles / p.tiles_m;
+  long g = s.c, b = s.iters;
+  while (b) { const long r = g % b; g = b; b = r; }
+  const int q = (int)(s.c / g);
+  if (n % q) return;
+  const int m = n / q;  // tiles of one K-phase group
+  int best = 1 << 30;
+  for (int br = 1; br <= p.tiles_m; ++br) {
+    if (p.tiles_m % br || n % br) continue;
+    const int bc = n / br;
+    if (cols % bc || (p.tiles_m / br) * (cols / bc) != 8) continue;
+    for (int gr = 1; gr <= br; ++gr) {
+      if (br % gr || m % gr) continue;
+      const int gc = m / gr;
+      if (bc % gc || (br / gr) * (bc / gc) != q || gr + gc >= best) continue;
+      best = gr + gc;
+      p.no_xcd = 2;
+      p.skm_base = s.dp_tiles;
+      p.skm_col0 = s.dp_tiles / p.tiles_m;
+      p.skm_br = br; p.skm_bc = bc; p.skm_q = q; p.skm_gr = gr; p.skm_gc = gc;
+    }
+  }
+}
+
 size_t partial_bytes(const Dims& D, long M, long N, long K) {
   if (D.dt != TP_BF16) return 0;
   const int sp = choose_splits(M, N, K);
@@ -552,6 +585,7 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
       p.tiles_n = cdiv(p.N, CfgBig::BN);
       p.group_m = 8;
       p.no_xcd = 1;
+      sk_place(p, s);
       p.splits = 1;
       hipLaunchKernelGGL((gemm_sk_kernel<CfgBig, AK, BKM, EPI, bf16_t, ROLE>), dim3(s.dp_tiles + s.units),
                          dim3(CfgBig::NT), 0, st, p, s);

@@ -53,7 +53,8 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
 
 
 # Launch plans at full size: stream-K over a partial last wave (with and
-# without whole waves before it, ragged M and N, 3 and 6 fragments per tile)
+# without whole waves before it, ragged M and N, 3 and 6 fragments per tile,
+# with and without the per-XCD placement of stream-K tiles)
 # and split-K. Rows sampled (first, last, scattered), every column, fp64
 # reference from the same bf16 operands; a second call must match bitwise.
 @pytest.mark.parametrize("M,N,K,ak,bk,plan", [
@@ -67,6 +68,9 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
     (2048, 10256, 1536, 1, 1, "dp+half"),  # 328 tiles: 8192 columns whole, 2064 (ragged) in 136 half tiles
     (2048, 12288, 1536, 0, 0, "dp+half"),  # M-contiguous A and N-contiguous B in the half tiles
     (2048, 10256, 1536, 0, 1, "dp+half"),
+    (2048, 6144, 12288, 1, 0, "sk"),   # the 175B FC1 shape: stream-K tiles placed as 2 x 12 blocks per XCD
+    (2048, 6128, 12288, 1, 1, "sk"),   # the same placement with a ragged last tile-column
+    (2048, 12288, 6144, 1, 0, "sk"),   # the 175B FC2 shape: a whole wave, then stream-K tiles in 4 x 4 blocks
     (2064, 8208, 6144, 0, 0, "sk"),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
     (2064, 8208, 6144, 0, 1, "sk"),
     (1040, 2832, 4096, 1, 0, "split"),  # 60 tiles: split-K
