@@ -392,7 +392,13 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn,
     return;
   }
   const int tiles = p.tiles_m * p.tiles_n;
-  if ((tiles & 7) == 0 && !p.no_xcd) L = (L & 7) * (tiles >> 3) + (L >> 3);  // same-XCD runs of tiles
+  if (!p.no_xcd) {
+    // same-XCD runs of tiles: block L runs on XCD x = L mod 8 as its i-th
+    // block (i = L / 8); XCD x takes the x-th run of consecutive tiles, runs
+    // of q = tiles / 8 tiles plus one for the first tiles mod 8 XCDs
+    const int x = L & 7, i = L >> 3, q = tiles >> 3, r = tiles & 7;
+    L = x * q + min(x, r) + i;
+  }
   const int per_group = p.group_m * p.tiles_n;
   const int grp = L / per_group, first = grp * p.group_m;
   const int gs = min(p.tiles_m - first, p.group_m);
