@@ -29,6 +29,9 @@
  *     caller; the library never allocates, frees or keeps them.
  *   - Element type is given by `dtype`: TP_BF16 (storage bf16, fp32
  *     accumulation) or TP_FP32 (fp32 throughout).
+ *   - GELU is the erf form x Phi(x); the kernels evaluate Phi with the
+ *     rational approximation of Abramowitz & Stegun 7.1.26 (within 3e-7 of
+ *     the exact Phi in fp32), for GELU and for GELU' = Phi + x phi.
  *   - `stream` is a hipStream_t (NULL = default stream). Work is enqueued
  *     asynchronously; nothing synchronizes the host.
  *   - Outputs and gradients are overwritten, never accumulated.
