@@ -285,6 +285,39 @@ __device__ __forceinline__ void split_scores(const uint4* Lh, const uint4* Ll, c
   }
 }
 
+// split_scores with the low part of X read per step from this lane's LDS
+// slots (xl_lds[64 ks], 16 bytes each) instead of registers.
+template <int KS>
+__device__ __forceinline__ void split_scores_lds(const uint4* Lh, const uint4* Ll, const LaneOff& lo,
+                                                 const uint4 (&xh)[KS], const uint4* xl_lds, f32x16_t (&acc)[2]) {
+  uint4 fh[2][2], fl[2][2], xl[2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    fh[0][bb] = frag16(Lh, lo, 0, bb);
+    fl[0][bb] = frag16(Ll, lo, 0, bb);
+  }
+  xl[0] = xl_lds[0];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        fh[cur ^ 1][bb] = frag16(Lh, lo, ks + 1, bb);
+        fl[cur ^ 1][bb] = frag16(Ll, lo, ks + 1, bb);
+      }
+      xl[cur ^ 1] = xl_lds[64 * (ks + 1)];
+    }
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      mma16(fh[cur][bb], xh[ks], acc[bb], bf16_t{});
+      mma16(fl[cur][bb], xh[ks], acc[bb], bf16_t{});
+      mma16(fh[cur][bb], xl[cur], acc[bb], bf16_t{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // acc[bb] += sum over KS steps of X_row . Y_row (one product), Y from LDS.
 template <int KS>
 __device__ __forceinline__ void row_products(const uint4* L, const LaneOff& lo, const uint4 (&x)[KS],
@@ -727,8 +760,8 @@ fa_bwd_dkv_kernel(const FaArgs a) {
 // ---------------------------------------------------------------------------
 // backward, dQ: items as in the forward pass
 // ---------------------------------------------------------------------------
-template <int D, int NBUF>
-__device__ __forceinline__ void fa_dq_body(const FaArgs& a, uint4* lds) {
+template <int D, int NBUF, bool QLDS = false>
+__device__ __forceinline__ void fa_dq_body(const FaArgs& a, uint4* lds, uint4* qlo_lds = nullptr) {
   constexpr int DP = (D + 63) / 64 * 64, KS = D / 16, NB = D / 32;
   using TL = fa::Tile<DP>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -759,6 +792,13 @@ __device__ __forceinline__ void fa_dq_body(const FaArgs& a, uint4* lds) {
   fa::settle(dof);
   fa::settle(lse);
   fa::settle(dsum);
+  // (single-buffered, two workgroups per CU: Q's low part waits in LDS, which
+  // frees its registers for the loop)
+  uint4* const xl_lds = QLDS ? qlo_lds + wave * KS * 64 + lane : nullptr;
+  if constexpr (QLDS) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xl_lds[64 * ks] = ql[ks];
+  }
   fa::LaneOff lo;
   lo.init(lane);
   TL tk, tl;
@@ -796,19 +836,32 @@ __device__ __forceinline__ void fa_dq_body(const FaArgs& a, uint4* lds) {
         fa::zero(sacc[bb]);
         fa::zero(dp[bb]);
       }
-      fa::split_scores<KS>(Lk, Lk + TL::U4, lo, qh, ql, sacc);
+      if constexpr (QLDS) fa::split_scores_lds<KS>(Lk, Lk + TL::U4, lo, qh, xl_lds, sacc);
+      else fa::split_scores<KS>(Lk, Lk + TL::U4, lo, qh, ql, sacc);
       fa::row_products<KS>(Lk + 2 * TL::U4, lo, dof, dp);  // dP = dC V^T
       // dS = P (dP - D) / sqrt(d), P = 0 for key > query or key >= s
       const bool edge = fa::BT * t + fa::BT - 1 > q0 + 32 * wave || fa::BT * t + fa::BT > a.s;
+      // (with Q's low part in LDS the registers allow a second, mask-free loop
+      // for tiles clear of the diagonal, as in the dK/dV kernel)
+      if (!QLDS || edge) {
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = fa::BT * t + fa::acc_col(bb, e, g);
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][e], a.sl2, -lse));
-          const float v = p * a.sc * (dp[bb][e] - dsum);
-          dp[bb][e] = (edge && (key > qrow || key >= a.s)) ? 0.0f : v;
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int key = fa::BT * t + fa::acc_col(bb, e, g);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][e], a.sl2, -lse));
+            const float v = p * a.sc * (dp[bb][e] - dsum);
+            dp[bb][e] = (edge && (key > qrow || key >= a.s)) ? 0.0f : v;
+          }
+      } else {  // clear of the diagonal and the sequence end: no mask
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][e], a.sl2, -lse));
+            dp[bb][e] = p * a.sc * (dp[bb][e] - dsum);
+          }
+      }
       fa::tr_products<NB>(Lk, lo, dp, dq);  // dQ += dS Kh
     }
   };
@@ -854,7 +907,8 @@ fa_bwd_dq_kernel(const FaArgs a) {
 template <int D>
 __global__ void __launch_bounds__(256, 2) fa_bwd_dq2_kernel(const FaArgs a) {
   __shared__ __attribute__((aligned(1024))) uint4 lds[3 * fa::Tile<(D + 63) / 64 * 64>::U4];
-  fa_dq_body<D, 1>(a, lds);
+  __shared__ __attribute__((aligned(16))) uint4 qlo[4 * (D / 16) * 64];
+  fa_dq_body<D, 1, true>(a, lds, qlo);
 }
 
 // Backward combine: grid (blocks * D / 8, z), one float4 per thread per
