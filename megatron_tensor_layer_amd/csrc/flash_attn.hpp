@@ -33,7 +33,8 @@
 //   fa_bwd_dkv_kernel: 128 keys (32 per wave); queries in tiles of 64 (Qh,
 //                      Ql, dC + LSE and D); accumulates dK, dV.
 //   fa_bwd_dq_kernel : 128 queries; keys in tiles of 64; dQ (fa_bwd_dq2_kernel:
-//                      single-buffered, two workgroups per CU).
+//                      single-buffered, two workgroups per CU, Q's low part
+//                      kept in LDS rather than registers).
 // dQ has its own kernel (recomputing P and dP) so that every gradient is a
 // fixed-order sum: no atomics, bitwise reproducible.
 //
