@@ -158,6 +158,50 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const T* __restrict__ dC, c
   }
 }
 
+// rowdot_kernel fused with the fixed-order split-K sum that produces dC (the
+// output projection's input gradient, split along K): per token row, each
+// 4-element chunk is the sum of the splits' fp32 partials (split order),
+// stored as bf16 dC, and the rounded values enter the same chunk products and
+// per-head sums as in rowdot_kernel, so D is bitwise the unfused result.
+// part: splits planes of T x (ar d) fp32; dC row pitch ar d.
+__global__ void __launch_bounds__(256) splitk_rowdot_kernel(const float* __restrict__ part, int splits,
+                                                            bf16_t* __restrict__ dC, const float* __restrict__ C,
+                                                            float* __restrict__ D, int T, int b, int ar, int d,
+                                                            int s) {
+  __shared__ float red[ROWDOT_LDS];
+  const int row = blockIdx.x;
+  const long ld = (long)ar * d;
+  const int cpd = d / 4;
+  const int hpp = ROWDOT_LDS / cpd;
+  const int sigma = row / b, beta = row - (row / b) * b;
+  for (int h0 = 0; h0 < ar; h0 += hpp) {
+    const int nh = min(hpp, ar - h0);
+    const int nc = nh * cpd;
+    for (int c = threadIdx.x; c < nc; c += 256) {
+      const long off = (long)row * ld + (long)h0 * d + 4 * c;
+      float u[4] = {0.f, 0.f, 0.f, 0.f}, v[4];
+      for (int k = 0; k < splits; ++k) {
+        float x[4];
+        Elt<float>::load4(part + (long)k * T * ld + off, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] += x[e];
+      }
+      Elt<bf16_t>::store4(dC + off, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = bf2f(f2bf(u[e]));
+      Elt<float>::load4(C + off, v);
+      red[c] = (u[0] * v[0] + u[1] * v[1]) + (u[2] * v[2] + u[3] * v[3]);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nh; j += 256) {
+      float acc = 0.0f;
+      for (int c = 0; c < cpd; ++c) acc += red[j * cpd + c];
+      D[((long)beta * ar + h0 + j) * s + sigma] = acc;
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // out[n] = sum_r X[r, n]: bias gradients in one fixed-order pass. A block owns
 // 8 x VEC columns (8 column threads of 16 bytes: a 128-byte row piece) over all

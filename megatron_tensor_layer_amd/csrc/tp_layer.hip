@@ -621,8 +621,15 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
 // A block's input-gradient GEMM (problem 0: dY W^T, K-contiguous operands,
 // epilogue E0) and weight-gradient GEMM (problem 1: X^T dY) in one launch
 // when both run on the direct bf16 kernel; otherwise two launches.
+// Attention backward: D = rowsum(dC * C) may ride on the split-K sum of dC.
+struct RowdotFuse {
+  const float* C;  // fp32 context [T, hr]
+  float* D;        // [b, a_r, s]
+};
+
 template <int E0, int ROLE, int ROLE0, int ROLE1>
-hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_t st) {
+hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_t st,
+                const RowdotFuse* rd = nullptr, bool* rd_done = nullptr) {
   using K0 = GemmKind<true, true, E0, bf16_t>;
   using K1 = GemmKind<false, false, EPI_LINEAR, bf16_t>;
   const bool direct = D.dt == TP_BF16 && direct_ok<CfgBig>(p0, 1) && direct_ok<CfgBig>(p1, 1);
@@ -655,9 +662,16 @@ hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_
   if (splits > 1) {
     hipLaunchKernelGGL((gemm_pair_kernel<CfgBig, GemmKind<true, true, EPI_PARTIAL, float>, K1, ROLE>),
                        dim3(units0 + tiles1), dim3(CfgBig::NT), 0, st, p0, p1, tiles0, units0, tiles1, first1);
-    const long n4 = (long)p0.M * p0.N / 4;
-    hipLaunchKernelGGL((splitk_reduce_kernel<E0, bf16_t, bf16_t, ROLE>), dim3((unsigned)cdivl(n4, 256)), dim3(256), 0,
-                       st, p0);
+    if (rd && E0 == EPI_LINEAR && !p0.bias && !p0.resid && p0.alpha == 1.0f && p0.M == D.T && p0.N == D.hr &&
+        p0.ldc == D.hr) {
+      hipLaunchKernelGGL(splitk_rowdot_kernel, dim3((unsigned)D.T), dim3(256), 0, st, part, splits,
+                         static_cast<bf16_t*>(p0.C), rd->C, rd->D, (int)D.T, (int)D.b, (int)D.ar, (int)D.d, (int)D.s);
+      if (rd_done) *rd_done = true;
+    } else {
+      const long n4 = (long)p0.M * p0.N / 4;
+      hipLaunchKernelGGL((splitk_reduce_kernel<E0, bf16_t, bf16_t, ROLE>), dim3((unsigned)cdivl(n4, 256)), dim3(256),
+                         0, st, p0);
+    }
   } else {
     hipLaunchKernelGGL((gemm_pair_kernel<CfgBig, K0, K1, ROLE>), dim3(units0 + tiles1), dim3(CfgBig::NT), 0, st, p0,
                        p1, tiles0, units0, tiles1, first1);
@@ -885,6 +899,7 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
   const float scale = (float)(1.0 / std::sqrt((double)D.d));
   const double es = (double)D.es, sde = (double)D.z * D.s * D.d * es;
 
+  bool rd_done = false;
   {  // dC = dH Wo_r^T
     GemmArgs p = gargs(D.T, D.hr, D.h);
     p.A = dy; p.lda = D.h;
@@ -895,10 +910,12 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     q.A = C; q.lda = D.hr;
     q.B = dy; q.ldb = D.h;
     q.C = g->dw_out; q.ldc = D.h;
-    TRY((pair<EPI_LINEAR, R_O_BWD, R_O_DGRAD, R_O_WGRAD>(D, p, q, part, st)));
+    // (a split-K dC also gives D = rowsum(dC * C) in its summing pass)
+    const RowdotFuse rdf{C32, Dv};
+    TRY((pair<EPI_LINEAR, R_O_BWD, R_O_DGRAD, R_O_WGRAD>(D, p, q, part, st, &rdf, &rd_done)));
   }
   TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, st));  // dbo (replica)
-  {  // D = rowsum(dC * C) per (sequence, head, query)
+  if (!rd_done) {  // D = rowsum(dC * C) per (sequence, head, query)
     prof::Scope sc(R_ROWDOT, 2.0 * D.T * D.hr, D.T * D.hr * (es + 4.0) + 4.0 * D.z * D.s, st);
     if (D.dt == TP_BF16) TRY(rowdot_t<bf16_t>(D, dC, C32, Dv, st));
     else TRY(rowdot_t<float>(D, dC, C32, Dv, st));
