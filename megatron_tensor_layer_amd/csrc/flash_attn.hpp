@@ -589,26 +589,41 @@ __global__ void __launch_bounds__(256) fa_fwd_combine_kernel(const FaArgs a) {
   const int wave = j / (NB * 256), rem = j - wave * (NB * 256), nb = rem >> 8, jj = (rem >> 6) & 3,
             lane = rem & 63;
   const int r = 32 * wave + (lane & 31), qrow = blk * fa::BQ + r;
-  if (qrow >= a.s) return;
-  const float2* ml = reinterpret_cast<const float2*>(a.part + fa::part_slot(a.z, 0, 0, a.s, a.ct, D));
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[fa::part_slot(z, blk, c, a.s, a.ct, 1) + r].x);
-  float L = 0.0f, v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nch; ++c) {
-    const float2 x = ml[fa::part_slot(z, blk, c, a.s, a.ct, 1) + r];
-    const float w = __builtin_amdgcn_exp2f(x.x - M);
-    L += w * x.y;
-    const float4 p = reinterpret_cast<const float4*>(a.part + fa::part_slot(z, blk, c, a.s, a.ct, D))[j];
-    v[0] += w * p.x; v[1] += w * p.y; v[2] += w * p.z; v[3] += w * p.w;
-  }
-  const float inv = 1.0f / L;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (qrow < a.s) {  // (rows past the sequence end: nothing to combine)
+    const float2* ml = reinterpret_cast<const float2*>(a.part + fa::part_slot(a.z, 0, 0, a.s, a.ct, D));
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[fa::part_slot(z, blk, c, a.s, a.ct, 1) + r].x);
+    float L = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+      const float2 x = ml[fa::part_slot(z, blk, c, a.s, a.ct, 1) + r];
+      const float w = __builtin_amdgcn_exp2f(x.x - M);
+      L += w * x.y;
+      const float4 p = reinterpret_cast<const float4*>(a.part + fa::part_slot(z, blk, c, a.s, a.ct, D))[j];
+      v[0] += w * p.x; v[1] += w * p.y; v[2] += w * p.z; v[3] += w * p.w;
+    }
+    const float inv = 1.0f / L;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] *= inv;
-  const long trow = (long)qrow * a.b + beta;
-  const int col = head * a.d + 32 * nb + 8 * jj + 4 * (lane >> 5);
-  Elt<bf16_t>::store4(a.ctx + trow * a.hr + col, v);
-  Elt<float>::store4(a.ctx32 + trow * a.hr + col, v);
-  if (nb == 0 && jj == 0 && lane < 32) a.lse[(long)z * a.s + qrow] = M + __log2f(L);
+    for (int e = 0; e < 4; ++e) v[e] *= inv;
+    if (nb == 0 && jj == 0 && lane < 32) a.lse[(long)z * a.s + qrow] = M + __log2f(L);
+  }
+  // The block's 1024 values are 32 rows x 32 columns; in register order a
+  // store instruction would write 16 bytes to each of 32 rows. Staged
+  // through LDS, 8 consecutive threads write one row's 32 columns.
+  __shared__ float4 st[32][8];
+  const int c4 = 2 * jj + (lane >> 5);
+  st[lane & 31][c4] = make_float4(v[0], v[1], v[2], v[3]);
+  __syncthreads();
+  const int rr = threadIdx.x >> 3, cc = threadIdx.x & 7;
+  const int qrow2 = blk * fa::BQ + 32 * wave + rr;
+  if (qrow2 < a.s) {
+    const float4 x = st[rr][cc];
+    const float w4[4] = {x.x, x.y, x.z, x.w};
+    const long trow2 = (long)qrow2 * a.b + beta;
+    const int col2 = head * a.d + 32 * nb + 4 * cc;
+    Elt<bf16_t>::store4(a.ctx + trow2 * a.hr + col2, w4);
+    Elt<float>::store4(a.ctx32 + trow2 * a.hr + col2, w4);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -928,18 +943,32 @@ __global__ void __launch_bounds__(256) fa_bwd_combine_kernel(const FaArgs a) {
   const int wave = j / (NB * 256), rem = j - wave * (NB * 256), nb = rem >> 8, jj = (rem >> 6) & 3,
             lane = rem & 63;
   const int row = blk * fa::BQ + 32 * wave + (lane & 31);
-  if (row >= a.s) return;
-  const long trow = (long)row * a.b + beta;
-  const int col = head * a.d + 32 * nb + 8 * jj + 4 * (lane >> 5);
+  // the block's values are 32 rows x 32 columns of each matrix; they are
+  // staged through LDS so that 8 consecutive threads store one row's 32
+  // columns (in register order a store would write 8 bytes to each of 32 rows)
+  __shared__ float4 st[32][8];
+  const int rr = threadIdx.x >> 3, cc = threadIdx.x & 7;
+  const int row2 = blk * fa::BQ + 32 * wave + rr;
+  const long trow2 = (long)row2 * a.b + beta;
+  const int col2 = head * a.d + 32 * nb + 4 * cc;
 #pragma unroll
   for (int mat = 0; mat < MATS; ++mat) {
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nch; ++c) {
-      const float4 x = reinterpret_cast<const float4*>(a.part + MATS * fa::part_slot(z, blk, c, a.s, a.ct, D) +
-                                                       mat * fa::BQ * D)[j];
-      v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+    if (row < a.s) {
+      for (int c = 0; c < nch; ++c) {
+        const float4 x = reinterpret_cast<const float4*>(a.part + MATS * fa::part_slot(z, blk, c, a.s, a.ct, D) +
+                                                         mat * fa::BQ * D)[j];
+        v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+      }
     }
-    Elt<bf16_t>::store4(a.dqkv + trow * a.q3 + (KEYS ? (1 + mat) * a.hr : 0) + col, v);
+    if (mat > 0) __syncthreads();  // the previous matrix's stores have read st
+    st[lane & 31][2 * jj + (lane >> 5)] = make_float4(v[0], v[1], v[2], v[3]);
+    __syncthreads();
+    if (row2 < a.s) {
+      const float4 x = st[rr][cc];
+      const float w4[4] = {x.x, x.y, x.z, x.w};
+      Elt<bf16_t>::store4(a.dqkv + trow2 * a.q3 + (KEYS ? (1 + mat) * a.hr : 0) + col2, w4);
+    }
   }
 }
 
