@@ -71,6 +71,8 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
     (2048, 6144, 12288, 1, 0, "sk"),   # the 175B FC1 shape: stream-K tiles placed as 2 x 12 blocks per XCD
     (2048, 6128, 12288, 1, 1, "sk"),   # the same placement with a ragged last tile-column
     (2048, 12288, 6144, 1, 0, "sk"),   # the 175B FC2 shape: a whole wave, then stream-K tiles in 4 x 4 blocks
+    (1024, 12288, 8192, 0, 1, "sk"),   # 4 tile-rows: 2 x 12 blocks per XCD, two blocks down the rows
+    (2048, 10240, 4096, 1, 1, "sk"),   # a whole wave, then 64 stream-K tiles in 2 x 4 blocks from column 32
     (2064, 8208, 6144, 0, 0, "sk"),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
     (2064, 8208, 6144, 0, 1, "sk"),
     (1040, 2832, 4096, 1, 0, "split"),  # 60 tiles: split-K
