@@ -24,7 +24,11 @@ and the backward with full activation recomputation ("recompute", counted
 with the page's 96 b s h^2 (1 + s/6h) per layer as well as by executed
 products).
 
+The other layer shapes (1.7B, 18B, 1T) are timed the same way, fewer steps,
+and reported under "shapes".
+
     python bench.py [--steps K] [--warmup W] [--config gpt_175b] [--no-cpu-baseline] [--no-modes]
+                    [--no-shapes]
 
 Prints one JSON line.  Only one GPU is used: --gpus above 1 is refused.
 """
@@ -344,53 +348,177 @@ def measure_sequence_parallel(layer, X, dY, cfg, steps, warmup):
     return out
 
 
-def cpu_baseline(cfg, target_s=15.0):
-    """The fp64 oracle (as it stands) on a bounded sample of the same
-    workload: rank 0's share of the layer, forward + backward of both blocks,
-    over the first L tokens of each sequence; FLOPs by the same formula."""
+def host_info():
+    """Host cores this process may use and the BLAS library numpy calls."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            d = libs[0]
+            blas = {"internal_api": d.get("internal_api"), "version": d.get("version"),
+                    "filepath": d.get("filepath"), "num_threads": d.get("num_threads")}
+    except Exception:  # pragma: no cover
+        pass
+    return {"host_cores": cores, "os_cpu_count": os.cpu_count(), "blas": blas}
+
+
+def _oracle_layer_pass(cfg, pr, ar, L, t_eff):
+    """One fwd + bwd pass of the oracle over the first L tokens of each
+    sequence: rank 0's share (t_eff = cfg.t, rank weights) or the unsharded
+    layer (t_eff = 1, full-width weights). Returns seconds."""
     import numpy as np
     from megatron_tensor_layer_amd import inputs as I
     from oracle import tp_layer_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    parts = I.params_rank(cfg, 0)
-    pr = {k: v.astype(np.float64) for k, v in parts.items()}
-    ar = cfg.a // cfg.t
-
-    def run(L):
-        T = L * cfg.b
-        X = I.activation(cfg, "X", tokens=T).astype(np.float64)
-        dY = I.activation(cfg, "dY", tokens=T).astype(np.float64)
-        t0 = time.perf_counter()
+    T = L * cfg.b
+    X = I.activation(cfg, "X", tokens=T).astype(np.float64)
+    dY = I.activation(cfg, "dY", tokens=T).astype(np.float64)
+    t0 = time.perf_counter()
+    if t_eff == 1:
+        Y, cache = O.layer_forward(X, pr, L, cfg.b, cfg.a)
+        O.layer_backward(cache, pr, dY, L, cfg.b, cfg.a)
+    else:
         pa, ca = O.attention_rank_forward(X, pr, L, cfg.b, ar)
         H = O.block_output([pa], pr["bo"], X)
         pm, cm = O.mlp_rank_forward(H, pr)
         gm = O.mlp_rank_backward(cm, pr, dY)
         dH = O.block_output([gm["dH"]], residual=dY)
         O.attention_rank_backward(ca, pr, dH, L, cfg.b, ar)
-        return time.perf_counter() - t0
+    return time.perf_counter() - t0
 
+
+def _timed_sample(cfg, pr, ar, t_eff, target_s):
+    """Doubles L from 64 until a pass takes target_s / 3 (or L = s); repeats
+    the last L to about target_s / 1.5 of CPU time. Returns (L, mean s, passes)."""
     L = 64
-    el = run(L)
+    el = _oracle_layer_pass(cfg, pr, ar, L, t_eff)
     while el < target_s / 3 and L * 2 <= cfg.s:
         L *= 2
-        el = run(L)
-    # when the whole sequence is reached early, repeat it until about
-    # target_s / 1.5 of CPU time has been measured at that L (mean per pass)
+        el = _oracle_layer_pass(cfg, pr, ar, L, t_eff)
     times = [el]
     while sum(times) < target_s / 1.5 and len(times) < 8:
-        times.append(run(L))
-    el = sum(times) / len(times)
+        times.append(_oracle_layer_pass(cfg, pr, ar, L, t_eff))
+    return L, sum(times) / len(times), len(times)
+
+
+def cpu_baseline(cfg, target_s=15.0):
+    """The fp64 oracle (as it stands) on bounded samples of the same
+    workload, fwd + bwd of both blocks over the first L tokens of each
+    sequence, FLOPs by the same formula:
+      * rank 0's share (the reported value; like for like with the GPU's
+        per-rank time);
+      * the unsharded layer (all t ranks' work in one pass; its weights are
+        rank 0's shards repeated t times along the split axes, which gives
+        the oracle the same work as the drawn unsharded weights);
+      * the fp32 check configuration on one BLAS thread."""
+    import numpy as np
+    from megatron_tensor_layer_amd import inputs as I
+
+    info = host_info()
+    threads = (info["blas"] or {}).get("num_threads") or info["host_cores"]
+    parts = I.params_rank(cfg, 0)
+    pr = {k: v.astype(np.float64) for k, v in parts.items()}
+    del parts
+    ar = cfg.a // cfg.t
+    L, el, passes = _timed_sample(cfg, pr, ar, cfg.t, target_s)
     flops = model_flops_per_rank(cfg.h, L, cfg.b, cfg.t)
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(el, 3), "passes": len(times),
-            "sample": f"rank 0 of t={cfg.t}, fwd+bwd of both blocks, first {L} of {cfg.s} tokens x b={cfg.b}, "
-                      f"mean of {len(times)} passes (numpy float64, {threads} BLAS threads); "
-                      f"FLOPs = 72 b L h^2 (1 + L/6h) / t"}
+    out = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "seconds": round(el, 3), "passes": passes,
+           "sample": f"rank 0 of t={cfg.t}, fwd+bwd of both blocks, first {L} of {cfg.s} tokens x b={cfg.b}, "
+                     f"mean of {passes} passes (numpy float64, {threads} BLAS threads); "
+                     f"FLOPs = 72 b L h^2 (1 + L/6h) / t",
+           "host": info}
+
+    # the unsharded layer: full-width weights from rank 0's shards
+    t = cfg.t
+    full = {}
+    for k in ("Wq", "Wk", "Wv", "W1"):
+        full[k] = np.tile(pr[k], (1, t))
+    for k in ("bq", "bk", "bv", "b1"):
+        full[k] = np.tile(pr[k], t)
+    for k in ("Wo", "W2"):
+        full[k] = np.tile(pr[k], (t, 1))
+    full["bo"], full["b2"] = pr["bo"], pr["b2"]
+    del pr
+    Lu, elu, pu = _timed_sample(cfg, full, cfg.a, 1, target_s * 2 / 3)
+    del full
+    fu = model_flops_per_rank(cfg.h, Lu, cfg.b, 1)
+    out["unsharded_layer"] = {
+        "value": round(fu / elu / 1e12, 4), "unit": "TFLOP/s", "seconds": round(elu, 3), "passes": pu,
+        "tokens": Lu * cfg.b,
+        "sample": f"whole layer (h={cfg.h}, a={cfg.a}, unsharded), fwd+bwd, first {Lu} of {cfg.s} tokens x "
+                  f"b={cfg.b}; FLOPs = 72 b L h^2 (1 + L/6h)"}
+
+    # the fp32 check configuration, single-threaded
+    chk = I.CONFIGS["check_fp32"]
+    pc = {k: v.astype(np.float64) for k, v in I.params_full(chk).items()}
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    try:
+        reps, tot = 0, 0.0
+        while tot < 1.0 and reps < 2000:
+            tot += _oracle_layer_pass(chk, pc, chk.a, chk.s, 1)
+            reps += 1
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    fc = model_flops_per_rank(chk.h, chk.s, chk.b, 1)
+    out["check_fp32_single_thread"] = {
+        "ms_per_pass": round(1e3 * tot / reps, 4), "passes": reps, "gflops": round(fc / (tot / reps) / 1e9, 3),
+        "sample": f"fp32 check configuration (h={chk.h}, a={chk.a}, s={chk.s}, b={chk.b}), whole layer unsharded, "
+                  "fwd+bwd, one BLAS thread"}
+    return out
+
+
+def measure_shape(name, steps, warmup):
+    """Per-rank throughput of another layer shape, same protocol as the
+    headline figure (stand-in reductions excluded), plus its dominant GEMM
+    role from one profiled step."""
+    import numpy as np
+    import torch
+    from megatron_tensor_layer_amd import inputs as I
+    from megatron_tensor_layer_amd import tplayer as tp
+
+    cfg = I.CONFIGS[name]
+    layer, X, dY = build_layer(cfg)
+    for _ in range(warmup):
+        layer.forward(X)
+        layer.backward(dY)
+    seg, _ = timed_steps(layer, X, dY, steps)
+    seg = np.array(seg)
+    rank_loops = seg[:, [0, 2, 4, 6]].sum(axis=1)
+    t_rank = float(np.mean(rank_loops)) / cfg.t
+    F = model_flops_per_rank(cfg.h, cfg.s, cfg.b, cfg.t)
+    tp.tp_prof_enable(True)
+    layer.forward(X)
+    layer.backward(dY)
+    tp.tp_prof_enable(False)
+    prof = tp.tp_prof_read()
+    gemm = {k: v for k, v in prof.items() if k not in NON_GEMM_ROLES}
+    dom = max(gemm, key=lambda k: gemm[k]["ms"])
+    de = prof[dom]
+    out = {"workload": f"{cfg.name} layer shard: h={cfg.h}, a={cfg.a}, s={cfg.s}, b={cfg.b}, t={cfg.t}",
+           "value": round(F / (t_rank * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+           "pct_of_peak": round(100.0 * F / (t_rank * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "rank_ms": round(t_rank, 4), "rank_ms_min": round(float(np.min(rank_loops)) / cfg.t, 4),
+           "steps": steps, "flops_per_rank": F,
+           "dominant": {"role": dom, "ms_per_launch": round(de["ms"] / de["launches"], 4),
+                        "tflops": round(de["flops"] / (de["ms"] * 1e-3) / 1e12, 1)}}
+    del layer, X, dY
+    torch.cuda.empty_cache()
+    return out
+
+
+NON_GEMM_ROLES = ("softmax", "rowdot", "reduce", "db1", "db2", "dbo", "dbqkv", "ln_fwd", "ln_bwd")
+OTHER_SHAPES = ("gpt_1.7b", "gpt_18b", "gpt_1t")
 
 
 def main():
@@ -402,6 +530,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the sequence-parallel LayerNorm and recompute measurements")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the other layer shapes (1.7B, 18B, 1T) reported under 'shapes'")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the t tensor-parallel ranks "
@@ -446,8 +576,7 @@ def main():
         roles[name] = {"launches": e["launches"], "ms_per_launch": round(e["ms"] / e["launches"], 4),
                        "tflops": round(e["flops"] / (e["ms"] * 1e-3) / 1e12, 1) if e["ms"] > 0 else None,
                        "gbps": round(e["bytes"] / (e["ms"] * 1e-3) / 1e9, 1) if e["ms"] > 0 else None}
-    gemm_roles = {k: v for k, v in prof.items() if k not in ("softmax", "rowdot", "reduce", "db1", "db2", "dbo",
-                                                              "dbqkv")}
+    gemm_roles = {k: v for k, v in prof.items() if k not in NON_GEMM_ROLES}
     dom = max(gemm_roles, key=lambda k: gemm_roles[k]["ms"])
     de = prof[dom]
     per_launch_ms = de["ms"] / de["launches"]
@@ -494,6 +623,11 @@ def main():
         n = max(3, args.steps // 2)
         out["sequence_parallel_layernorm"] = measure_sequence_parallel(layer, X, dY, cfg, n, 1)
         out["recompute"] = measure_recompute(layer, X, dY, cfg, n, 1)
+    if not args.no_shapes:
+        del layer, X, dY
+        torch.cuda.empty_cache()
+        n = max(3, args.steps // 4)
+        out["shapes"] = {name: measure_shape(name, n, 2) for name in OTHER_SHAPES if name != cfg.name}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     else:

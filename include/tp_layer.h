@@ -57,7 +57,9 @@ enum tp_block { TP_ATTN = 0, TP_MLP = 1 };
 enum tp_status {
   TP_OK = 0,
   TP_EINVAL = -1,        /* non-positive dims, h % a, a % t (heads stay whole), rank not in [0,t), bad enum */
-  TP_EUNSUPPORTED = -2,  /* s, b*s, d or h/t not a multiple of 16 */
+  TP_EUNSUPPORTED = -2,  /* s, b*s, d or h/t not a multiple of 16, or a matrix of
+                            2^31 or more elements (the tile loaders use 32-bit
+                            byte offsets within an operand) */
   TP_ENULL = -3,         /* a required pointer is NULL */
   TP_EALIGN = -4,        /* a pointer is not 16-byte aligned */
   TP_EWORKSPACE = -5,    /* workspace_bytes < tp_workspace_bytes(...) */
@@ -86,22 +88,37 @@ typedef struct {
 } tp_block_grads;
 
 /* Pure host validation, no HIP call: TP_OK or TP_EINVAL / TP_EUNSUPPORTED.
- * Heads must divide evenly by t ("parallelism" blog, Attention). */
+ * Heads must divide evenly by t ("parallelism" blog, Attention). Every
+ * matrix of the call must hold fewer than 2^31 elements: [T, h], [T, 4h/t],
+ * the weight shards (up to [h, 4h/t]) and, on the materialised attention
+ * path (fp32, or d not in {64, 96, 128, 160}), one [s, s] score matrix.   */
 int tp_check_args(int h, int a, int s, int b, int t, int rank, int dtype, int block);
 
 /* Bytes of activations that tp_layer_fwd(block, rank) saves for
- * tp_layer_bwd(block, rank). ATTN keeps QKV_r [T,3h/t] and the context C_r
+ * tp_layer_bwd(block, rank) (what the backward reads of the forward: the
+ * activation memory per layer of the interview book "Distributed training",
+ * section 2.2, for one rank's shards). ATTN keeps QKV_r [T,3h/t] and the context C_r
  * [T,h/t] (also in fp32 for bf16); with bf16 and d in {64, 96, 128, 160}
  * (fused attention) also the bf16 rounding residuals of Q_r and K_r [T,2h/t]
  * and one log-sum-exp per query and head, otherwise the causal softmax P_r
  * [b*a_r, s, s]. MLP keeps U_r and Z_r [T,4h/t]. 0 on invalid arguments. */
 size_t tp_saved_bytes(int h, int a, int s, int b, int t, int dtype, int block);
 
-/* Scratch bytes needed by both tp_layer_fwd and tp_layer_bwd of `block`
- * (score matrix, gradient temporaries, split-K partials). 0 on invalid args. */
+/* Scratch bytes needed by both tp_layer_fwd and tp_layer_bwd of `block`:
+ * the gradient temporaries of the chain rule ("parallelism" blog, "The
+ * backward pass": dC, D = rowsum(dC * C), dQKV for ATTN; dU for MLP), the
+ * score matrix of the materialised attention path, and fp32 partial tiles
+ * of split-K / stream-K GEMMs and of the fused attention's chunks. Owned by
+ * the caller, 16-byte aligned; its contents do not outlive a call, so one
+ * buffer of the larger of the two blocks' sizes serves every call on a
+ * stream. 0 on invalid args.                                                */
 size_t tp_workspace_bytes(int h, int a, int s, int b, int t, int dtype, int block);
 
-/* Forward of rank `rank`'s share of `block`.
+/* Forward of rank `rank`'s share of `block` (paper-graph page, section 3,
+ * "Tensor Model Parallelism: The Megatron Partitioning": the first GEMM of a
+ * block split by columns, the second by rows, so the block ends in a partial
+ * sum that the g all-reduce adds up; "parallelism" blog, "The MLP, with real
+ * numbers" and "Attention").
  *   x          [T, h]  block input, replicated on every rank (f = identity)
  *   w          rank-local weights (see tp_block_weights)
  *   y_partial  [T, h]  out: this rank's partial C_r Wo_r (ATTN) or Z_r W2_r
@@ -114,7 +131,9 @@ int tp_layer_fwd(int h, int a, int s, int b, int t, int rank, int dtype, int blo
                  const void *x, const tp_block_weights *w, void *y_partial, void *saved,
                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* Backward of rank `rank`'s share of `block`.
+/* Backward of rank `rank`'s share of `block` ("parallelism" blog, "The
+ * backward pass": weight gradients are local to the rank; the input
+ * gradient is a partial sum that f's backward all-reduce adds up).
  *   x, w       as passed to tp_layer_fwd
  *   saved      as written by tp_layer_fwd(block, rank), unchanged
  *   dy         [T, h] gradient of the block output, replicated (g's backward
@@ -209,7 +228,8 @@ int tp_layernorm_bwd(int dtype, long rows, long h, const void *dy, const void *v
  *   b_kmajor: B stored [N, ldb] (element (k,n) at B[n*ldb+k]) if 1, else
  *             stored [K, ldb] (element (k,n) at B[k*ldb+n]).
  *   bias may be NULL. C has leading dimension ldc. M, N, K multiples of 16;
- *   leading dimensions multiples of 8.
+ *   leading dimensions multiples of 8 (TP_EUNSUPPORTED otherwise, and when
+ *   A, B or C spans 2^31 or more elements, rows x leading dimension).
  *   workspace: device scratch of at least tp_gemm_workspace_bytes(dtype, M,
  *   N, K) bytes, 256-byte aligned, owned by the caller (NULL when that size is
  *   0); TP_EWORKSPACE if smaller. Used by the tests to check each operand

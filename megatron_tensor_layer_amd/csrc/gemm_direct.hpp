@@ -65,16 +65,12 @@ __device__ __forceinline__ uint2 read_tr(const uint4* lds, uint32_t byte_off) {
 
 // One operand's tile loader + fragment reader. R = rows of the operand tile
 // along M (or N); KMAJ = operand stored K-contiguous in HBM.
-#ifndef TPL_KSWZ
-#define TPL_KSWZ 1
-#endif
 // XOR swizzle of the 16-byte chunks of K-contiguous LDS row `row`: distinct for
 // any 8 consecutive rows, and for the 8 even (odd) rows of any 16, so that a
 // ds_read_b128 of 32 consecutive rows is bank-conflict free whether the LDS
 // serves 8 or 16 lanes per cycle.
 __device__ __forceinline__ int kswz(int row) {
-  if constexpr (TPL_KSWZ) return ((row >> 1) ^ ((row & 1) << 2)) & 7;
-  else return row & 7;
+  return ((row >> 1) ^ ((row & 1) << 2)) & 7;
 }
 
 // Segment swizzle of M/N-contiguous rows: segment ^ tsw(k). The four k rows a
@@ -149,34 +145,11 @@ struct DirectOperand {
   }
 };
 
-#ifndef TPL_DIRECT_SCHED
-#define TPL_DIRECT_SCHED 0
-#endif
-
-#ifndef TPL_DIRECT_FENCE
-#define TPL_DIRECT_FENCE 1
-#endif
-#ifndef TPL_DMA_SPREAD
-#define TPL_DMA_SPREAD 0
-#endif
-#ifndef TPL_SLOTS
-#define TPL_SLOTS 1
-#endif
-#ifndef TPL_SLOT_DMA_SUBS
-#define TPL_SLOT_DMA_SUBS 2
-#endif
-#ifndef TPL_SLOT_EARLY
-#define TPL_SLOT_EARLY 1
-#endif
-#ifndef TPL_DMA_EVERY
-#define TPL_DMA_EVERY 2
-#endif
-
 // One output tile: linear tile index L (ordered by tile_coords), split-K
 // piece `split`, batch z. LDS buffers are passed in (two per operand).
 // EPI_SK_PART: K range [kb_, ke_) and the fp32 fragment goes to skdst as a
 // row-major BM x BN tile.
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int KSEG, bool SCHED, bool FENCE>
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int KSEG>
 __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split, int z, uint4* sa0, uint4* sb0,
                                             uint4* sa1, uint4* sb1, int kb_ = 0, int ke_ = 0,
                                             float* skdst = nullptr) {
@@ -255,17 +228,21 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // One K tile from LDS (As, Bs) while the next tile's loads (issue_next)
-  // are in flight. Each sub-step is a scheduling region: the next
-  // sub-step's fragment reads go first, then the MFMAs (sub-step 0 pairs
-  // the tile's global->LDS loads one per MFMA), so at most two sub-steps of
-  // fragments are live and every read has 16 MFMAs to land.
-  constexpr int NRD = (AK ? TM : 2 * TM) + (BKM ? TN : 2 * TN);  // LDS reads per sub-step
+  // Main loop. A K tile is four 16-deep sub-steps of MF = TM x TN MFMAs per
+  // wave. Each sub-step is written out as MF slots in program order, one
+  // MFMA per slot, with a scheduling barrier after each slot: the next
+  // sub-step's NR fragment reads (A, then B) are spread one per slot at a
+  // stride of MF / NR, and the global->LDS loads of the next tile one per
+  // slot at a stride of MF / DPS, half a stride later. Fragment registers
+  // alternate between two sets by sub-step, so every read has a whole
+  // sub-step of MFMAs to land.
+  //
+  // Software pipeline across the per-tile barrier: the first DPS loads of
+  // tile kt + 1 go out during sub-step 3 of tile kt - 1 (right after that
+  // tile's barrier, into the buffers it has just freed), the other NLD - DPS
+  // during sub-step 0 of tile kt. Sub-step 3 of tile kt runs after the
+  // barrier, while the first fragment reads of tile kt + 1 are in flight.
   constexpr int MF = TM * TN;
-  // Software pipeline across the per-tile barrier: the MFMAs of a tile's last
-  // sub-step run after the barrier, while the first fragment reads of the
-  // next tile are in flight. Fragment registers alternate between two sets
-  // by sub-step; sub-step 3 and the next tile's sub-step 0 use different sets.
   uint4 af[2][TM], bq[2][TN];
   auto read_frags = [&](const uint4* As, const uint4* Bs, int ks, int set) {
 #pragma unroll
@@ -273,19 +250,8 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 #pragma unroll
     for (int j = 0; j < TN; ++j) bq[set][j] = ob.frag(Bs, wn * WTN + j * 32, ks, lane);
   };
-  auto mfmas = [&](int set) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int i = 0; i < TM; ++i) mma16(bq[set][j], af[set][i], acc[i][j], bf16_t{});
-  };
   constexpr int NLD = OA::PER_WAVE + OB::PER_WAVE;  // global->LDS loads per tile and wave
-  // One sub-step as MF slots in program order. Slot q issues MFMA q (set
-  // set_mma); the sub-step's NR fragment reads (k step ks_rd into set_rd: A
-  // fragments, then B) go one per slot from slot 0 at a stride of MF / NR;
-  // the DPS next-tile loads dq0.. go one per slot at a stride of MF / DPS,
-  // half a stride later.
-  constexpr int NR = TM + TN, DPS = (NLD + TPL_SLOT_DMA_SUBS - 1) / TPL_SLOT_DMA_SUBS;
+  constexpr int NR = TM + TN, DPS = (NLD + 1) / 2;
   auto slot_step = [&](int set_mma, const uint4* Ar, const uint4* Br, int ks_rd, int set_rd, int dq0,
                        const bf16_t* na, const bf16_t* nb, uint4* la, uint4* lb) {
 #pragma unroll
@@ -310,38 +276,12 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // MFMAs of one sub-step with the next tile's loads dq0, dq0+1, ... placed
-  // one after every DMA_EVERY MFMAs.
-  auto mfmas_dma = [&](int set, int dq0, const bf16_t* na, const bf16_t* nb, uint4* la, uint4* lb) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        mma16(bq[set][j], af[set][i], acc[i][j], bf16_t{});
-        const int q = j * TM + i;
-        if ((q % TPL_DMA_EVERY) == TPL_DMA_EVERY - 1) {
-          const int d = dq0 + q / TPL_DMA_EVERY;
-          if (d < OA::PER_WAVE) oa.issue_one(na, la, wave, d);
-          else if (d < NLD) ob.issue_one(nb, lb, wave, d - OA::PER_WAVE);
-        }
-      }
-  };
-  auto interleave = [&]() {
-    if constexpr (FENCE) {
-      sched_pairs<(NRD < MF ? NRD : MF), 0x100>();
-      if constexpr (MF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, MF - NRD, 0);
-    }
-  };
-  auto fence = [&]() {
-    if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
-  };
 
   // Past the last tile the prefetch repeats the last tile into the idle
   // buffer (in bounds, never read), keeping the loop free of divergence.
   if (nk > 0) issue(0, sa0, sb0);
   wait_loads();
   __syncthreads();
-#if TPL_SLOTS && TPL_SLOT_EARLY
   if (nk > 1) {
     const bf16_t *na, *nb;
     next_ptrs(1, na, nb);
@@ -351,7 +291,6 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
       else if (d < NLD) ob.issue_one(nb, sb1, wave, d - OA::PER_WAVE);
     }
   }
-#endif
   if (nk > 0) read_frags(sa0, sb0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const bool odd = kt & 1;
@@ -359,11 +298,6 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     const uint4* Bs = odd ? sb1 : sb0;
     uint4* An = odd ? sa0 : sa1;
     uint4* Bn = odd ? sb0 : sb1;
-#if TPL_SLOTS && TPL_SLOT_EARLY
-    // The first DPS loads of tile kt + 1 went out right after the previous
-    // barrier; sub-step 0 issues the rest. After this tile's barrier its own
-    // buffers are free (sub-step 3 fragments are in registers), so the first
-    // loads of tile kt + 2 go into them during sub-step 3.
     const bf16_t *na, *nb;
     next_ptrs(min(kt + 1, nk - 1), na, nb);
     slot_step(0, As, Bs, 1, 1, DPS, na, nb, An, Bn);
@@ -375,65 +309,9 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     // (near the end the clamped index repeats tile nk - 1 into a buffer no
     // later fragment read uses; in bounds, drained after the loop)
     slot_step(1, An, Bn, 0, 0, 0, na, nb, const_cast<uint4*>(As), const_cast<uint4*>(Bs));
-#elif TPL_SLOTS
-    const bf16_t *na, *nb;
-    next_ptrs(min(kt + 1, nk - 1), na, nb);
-    slot_step(0, As, Bs, 1, 1, 0, na, nb, An, Bn);          // sub-step 0, loads 0..
-    slot_step(1, As, Bs, 2, 0, DPS, na, nb, An, Bn);        // sub-step 1, loads DPS..
-    slot_step(0, As, Bs, 3, 1, 2 * DPS, na, nb, An, Bn);    // sub-step 2
-    wait_loads();
-    __syncthreads();
-    slot_step(1, An, Bn, 0, 0, NLD, na, nb, An, Bn);       // sub-step 3 + next tile's first reads
-#else
-#if TPL_DMA_SPREAD
-    constexpr int PER_SUB = MF / TPL_DMA_EVERY;  // loads per sub-step
-    const bf16_t *na, *nb;
-    next_ptrs(min(kt + 1, nk - 1), na, nb);
-    fence();
-    read_frags(As, Bs, 1, 1);  // sub-step 0: MFMAs on set 0, reads of sub-step 1, next tile's loads
-    mfmas_dma(0, 0, na, nb, An, Bn);
-    fence();
-    read_frags(As, Bs, 2, 0);  // sub-step 1
-    mfmas_dma(1, PER_SUB, na, nb, An, Bn);
-    if constexpr (2 * PER_SUB < NLD) {
-      fence();
-      read_frags(As, Bs, 3, 1);  // sub-step 2
-      mfmas_dma(0, 2 * PER_SUB, na, nb, An, Bn);
-    } else {
-      fence();
-      read_frags(As, Bs, 3, 1);  // sub-step 2
-      mfmas(0);
-      interleave();
-    }
-#else
-    fence();
-    read_frags(As, Bs, 1, 1);  // sub-step 0: MFMAs on set 0, reads of sub-step 1, next tile's loads
-    mfmas(0);
-    issue(min(kt + 1, nk - 1), An, Bn);
-    interleave();
-    fence();
-    read_frags(As, Bs, 2, 0);  // sub-step 1
-    mfmas(1);
-    interleave();
-    fence();
-    read_frags(As, Bs, 3, 1);  // sub-step 2
-    mfmas(0);
-    interleave();
-#endif
-    fence();
-    wait_loads();
-    __syncthreads();
-    // sub-step 3 of this tile after the barrier, with sub-step 0 of the next
-    // tile's reads (the last iteration reads the idle buffer: in bounds, unused)
-    read_frags(An, Bn, 0, 0);
-    mfmas(1);
-    interleave();
-#endif
   }
-#if TPL_SLOTS && TPL_SLOT_EARLY
   wait_loads();
-#endif
-  fence();
+  __builtin_amdgcn_sched_barrier(0);
 
   // Epilogue through LDS. Stored straight from the MFMA layout, a lane holds
   // 4 columns of one row and a store instruction touches 32 rows, which
@@ -492,27 +370,25 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   uint4* const sa1 = lds_ + ((BM) + (BN)) * 8;                              \
   uint4* const sb1 = lds_ + (2 * (BM) + (BN)) * 8;
 
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1, bool SCHED = TPL_DIRECT_SCHED,
-          bool FENCE = TPL_DIRECT_FENCE>
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256)))
 gemm_direct_kernel(const GemmArgs p) {
   TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
-  direct_tile<Cfg, AK, BKM, EPI, TO, KSEG, SCHED, FENCE>(p, blockIdx.x, blockIdx.y, blockIdx.z, sa0, sb0, sa1, sb1);
+  direct_tile<Cfg, AK, BKM, EPI, TO, KSEG>(p, blockIdx.x, blockIdx.y, blockIdx.z, sa0, sb0, sa1, sb1);
 }
 
 // Stream-K launch (plan in SkPlan). Consecutive blocks go to different XCDs,
 // so block b is remapped to (b mod 8) * (n / 8) + b / 8: each XCD takes one
 // contiguous run of whole tiles and one contiguous run of stream-K units,
 // and the tiles of a run share operand panels in that XCD's L2.
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, bool SCHED = TPL_DIRECT_SCHED,
-          bool FENCE = TPL_DIRECT_FENCE>
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256)))
 gemm_sk_kernel(const GemmArgs p, const SkPlan s) {
   TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
   const int b = blockIdx.x;
   if (b < s.dp_tiles) {
     const int L = (b & 7) * (s.dp_tiles >> 3) + (b >> 3);
-    direct_tile<Cfg, AK, BKM, EPI, TO, 1, SCHED, FENCE>(p, L, 0, 0, sa0, sb0, sa1, sb1);
+    direct_tile<Cfg, AK, BKM, EPI, TO, 1>(p, L, 0, 0, sa0, sb0, sa1, sb1);
     return;
   }
   const int sb = b - s.dp_tiles;
@@ -526,7 +402,7 @@ gemm_sk_kernel(const GemmArgs p, const SkPlan s) {
     const int k1 = (int)min((long)s.iters, k0 + (end - it));
     const int slot = u - (int)(((long)j * s.iters) / s.c);
     float* dst = s.part + ((long)j * s.f + slot) * (long)(Cfg::BM * Cfg::BN);
-    direct_tile<Cfg, AK, BKM, EPI_SK_PART, float, 1, SCHED, FENCE>(p, s.dp_tiles + j, 0, 0, sa0, sb0, sa1, sb1,
+    direct_tile<Cfg, AK, BKM, EPI_SK_PART, float, 1>(p, s.dp_tiles + j, 0, 0, sa0, sb0, sa1, sb1,
                                                                    k0 * 64, k1 * 64, dst);
     it += k1 - k0;
     __syncthreads();  // the next run's first loads reuse this run's LDS buffers
@@ -572,7 +448,7 @@ struct GemmKind {
 // which problem's blocks come first. The host puts the longer K per tile
 // first, so the long tiles start first and the short ones fill in around
 // them (longest-processing-time order over the 256 CUs).
-template <class Cfg, class K0, class K1, int ROLE, bool SCHED = TPL_DIRECT_SCHED, bool FENCE = TPL_DIRECT_FENCE>
+template <class Cfg, class K0, class K1, int ROLE>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256)))
 gemm_pair_kernel(const GemmArgs p0, const GemmArgs p1, int tiles0, int units0, int tiles1, int first1) {
   TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
@@ -582,10 +458,10 @@ gemm_pair_kernel(const GemmArgs p0, const GemmArgs p1, int tiles0, int units0, i
   if (first1) u = is0 ? u - tiles1 : u + units0;
   if (is0) {
     const int split = u / tiles0;
-    direct_tile<Cfg, K0::AK, K0::BK, K0::EPI, typename K0::TO, 1, SCHED, FENCE>(p0, u - split * tiles0, split, 0, sa0,
+    direct_tile<Cfg, K0::AK, K0::BK, K0::EPI, typename K0::TO, 1>(p0, u - split * tiles0, split, 0, sa0,
                                                                                  sb0, sa1, sb1);
   } else {
-    direct_tile<Cfg, K1::AK, K1::BK, K1::EPI, typename K1::TO, 1, SCHED, FENCE>(p1, u - units0, 0, 0, sa0, sb0, sa1,
+    direct_tile<Cfg, K1::AK, K1::BK, K1::EPI, typename K1::TO, 1>(p1, u - units0, 0, 0, sa0, sb0, sa1,
                                                                                  sb1);
   }
 }

@@ -133,6 +133,10 @@ struct Dims {
   size_t es;
 };
 
+// Largest matrix (elements) a kernel may address: byte offsets of bf16
+// operands from their origin stay below 2^32.
+constexpr long kMaxElems = 1L << 31;
+
 int check_args(long h, long a, long s, long b, long t, long rank, int dt, int blk) {
   if (h <= 0 || a <= 0 || s <= 0 || b <= 0 || t <= 0) return TP_EINVAL;
   if (dt != TP_BF16 && dt != TP_FP32) return TP_EINVAL;
@@ -143,6 +147,15 @@ int check_args(long h, long a, long s, long b, long t, long rank, int dt, int bl
   if (s % 16 != 0 || d % 16 != 0 || hr % 16 != 0) return TP_EUNSUPPORTED;
   // rows and columns are 32-bit in the kernels; batch counts fit a grid dimension
   if (s * b > (1L << 30) || 4 * h > (1L << 30) || b * (a / t) > 65535) return TP_EUNSUPPORTED;
+  // The tile loaders address an operand with 32-bit byte offsets from its
+  // origin, so every matrix the layer reads or writes holds fewer than 2^31
+  // elements: activations [T, h] and [T, 4h/t], weight shards up to
+  // [h, 4h/t], and on the materialised attention path (fp32, or head widths
+  // the fused kernels are not built for) one sequence's [s, s] matrix.
+  const long T = s * b, fr = 4 * h / t;
+  if (T * h >= kMaxElems || T * fr >= kMaxElems || h * fr >= kMaxElems) return TP_EUNSUPPORTED;
+  const bool fused = dt == TP_BF16 && (d == 64 || d == 96 || d == 128 || d == 160);
+  if (!fused && s * s >= kMaxElems) return TP_EUNSUPPORTED;
   return TP_OK;
 }
 
@@ -158,11 +171,8 @@ Dims make_dims(long h, long a, long s, long b, long t, int dt) {
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Tile configurations.
-#ifndef TPL_BIG_WN
-#define TPL_BIG_WN 2
-#endif
-using CfgBig = TileCfg<bf16_t, 256, 256, 2, TPL_BIG_WN>;  // linear GEMMs
-using CfgB192 = TileCfg<bf16_t, 192, 256, 2, TPL_BIG_WN>;  // linear GEMMs of one partial wave
+using CfgBig = TileCfg<bf16_t, 256, 256, 2, 2>;  // linear GEMMs
+using CfgB192 = TileCfg<bf16_t, 192, 256, 2, 2>;  // linear GEMMs of one partial wave
 using CfgHalf = TileCfg<bf16_t, 256, 128, 2, 2>;              // the columns past whole waves
 using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
 using CfgF32 = TileCfg<float, 64, 64, 2, 2>;     // fp32 configuration
@@ -190,8 +200,9 @@ int att_tile(int dt) { return dt == TP_BF16 ? CfgMid::BM : CfgF32::BM; }
 // configuration materialise the causal s x s matrices with the GEMM kernels.
 bool flash(const Dims& D) {
   if (D.dt != TP_BF16) return false;
-  if (D.d != 64 && D.d != 96 && D.d != 128 && D.d != 160) return false;
-  return (double)D.T * D.q3 * 2.0 < 4294967296.0;  // 32-bit byte offsets of the tile loads
+  // (check_args keeps [T, 3h/t] below 2^31 elements, as the tile loads' 32-bit
+  // byte offsets need)
+  return D.d == 64 || D.d == 96 || D.d == 128 || D.d == 160;
 }
 
 // Flash attention chunk size: when the heads' query
@@ -243,16 +254,15 @@ SavedLayout saved_layout(const Dims& D, int blk) {
   return L;
 }
 
-#ifndef TPL_SK_MIN_TILES
-#define TPL_SK_MIN_TILES 160
-#endif
+// Fewest tiles for which stream-K over a lone partial wave pays.
+constexpr long kSkMinTiles = 160;
 // Stream-K plan for a bf16 GEMM on 256x256 tiles with whole 64-deep K steps
 // (units = 0: not worth it). Whole waves of tiles run as they are; the last,
 // partial wave's K iterations are spread over all 256 CUs. Without a whole
 // wave in front, the pieces start at staggered K offsets, so no two CUs of
 // an XCD share an operand slice in L2 and every piece's panels come from
 // beyond L2 (measured: 10x the operand bytes for a 144-tile GEMM); below
-// TPL_SK_MIN_TILES tiles a partial wave of whole tiles wins instead. Chosen when the
+// kSkMinTiles tiles a partial wave of whole tiles wins instead. Chosen when the
 // modelled time beats the plain (or split-K) launch; the model counts one
 // tile-iteration as ~1.95 us and charges the fp32 fragments' write + read at
 // ~5 TB/s plus a launch gap for the fix-up.
@@ -263,7 +273,7 @@ SkPlan sk_plan(long M, long N, long K) {
   const long I = K / CfgBig::BK;
   const long W = tiles / 256, R = tiles % 256;
   if (R == 0 || I < 8) return s;
-  if (W == 0 && tiles < TPL_SK_MIN_TILES) return s;  // too few tiles: a partial wave of whole tiles
+  if (W == 0 && tiles < kSkMinTiles) return s;  // too few tiles: a partial wave of whole tiles
   const double t_it = 1.95e-6, frag = 4.0 * CfgBig::BM * CfgBig::BN;
   double plain = (double)cdivl(tiles, 256) * I * t_it;
   const int sp = choose_splits(M, N, K);
@@ -1273,6 +1283,11 @@ int tp_gemm(int dtype, int M, int N, int K, float alpha, const void* A, long lda
   if (M <= 0 || N <= 0 || K <= 0) return TP_EINVAL;
   if (M % 16 || N % 16 || K % 16 || lda % 8 || ldb % 8 || ldc % 8) return TP_EUNSUPPORTED;
   if (lda < (a_kmajor ? K : M) || ldb < (b_kmajor ? K : N) || ldc < N) return TP_EINVAL;
+  // each operand and the output span fewer than 2^31 elements (32-bit byte
+  // offsets in the tile loaders)
+  if ((long)(a_kmajor ? M : K) * lda >= kMaxElems || (long)(b_kmajor ? N : K) * ldb >= kMaxElems ||
+      (long)M * ldc >= kMaxElems)
+    return TP_EUNSUPPORTED;
   if (!A || !B || !C) return TP_ENULL;
   if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias)) return TP_EALIGN;
   const Dims D = make_dims(16, 1, 16, 1, 1, dtype);  // only the dtype is used
@@ -1351,7 +1366,8 @@ const char* tp_strerror(int code) {
   switch (code) {
     case TP_OK: return "ok";
     case TP_EINVAL: return "invalid argument (dims, heads not divisible by t, rank out of range, or bad enum)";
-    case TP_EUNSUPPORTED: return "unsupported shape (s, d and h/t must be multiples of 16)";
+    case TP_EUNSUPPORTED:
+      return "unsupported shape (s, d and h/t must be multiples of 16; every matrix below 2^31 elements)";
     case TP_ENULL: return "a required pointer is NULL";
     case TP_EALIGN: return "a pointer is not 16-byte aligned";
     case TP_EWORKSPACE: return "workspace smaller than tp_workspace_bytes()";

@@ -50,6 +50,18 @@ def test_library_exports_every_declared_symbol():
     ((64, 4, 24, 2, 4, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EUNSUPPORTED),  # s % 16
     ((96, 4, 32, 2, 4, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EUNSUPPORTED),  # d = 24
     ((128, 8, 32, 2, 8, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_OK),           # d = 16, h/t = 16
+    # every matrix below 2^31 elements (32-bit byte offsets in the tile loaders)
+    ((32768, 256, 2048, 1, 1, 0, tp.TP_BF16, tp.TP_MLP), tp.TP_EUNSUPPORTED),   # W1 shard 32768 x 131072
+    ((32768, 256, 2048, 1, 4, 0, tp.TP_BF16, tp.TP_MLP), tp.TP_OK),             # W1 shard 32768 x 32768
+    ((16384, 128, 2048, 64, 8, 0, tp.TP_BF16, tp.TP_ATTN), tp.TP_EUNSUPPORTED),  # X: 131072 x 16384 = 2^31
+    ((16384, 128, 2048, 32, 8, 0, tp.TP_BF16, tp.TP_ATTN), tp.TP_OK),            # X: 2^30
+    ((4096, 32, 8192, 2, 8, 0, tp.TP_BF16, tp.TP_MLP), tp.TP_OK),
+    ((4096, 32, 8192, 16, 1, 0, tp.TP_BF16, tp.TP_MLP), tp.TP_EUNSUPPORTED),    # U: 131072 x 16384
+    # one [s, s] score matrix on the materialised path (fp32, or d = 48); none on the fused bf16 path
+    ((1024, 8, 47104, 1, 1, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_EUNSUPPORTED),   # 47104^2 > 2^31
+    ((1024, 8, 46336, 1, 1, 0, tp.TP_FP32, tp.TP_ATTN), tp.TP_OK),             # 46336^2 < 2^31
+    ((1024, 8, 47104, 1, 1, 0, tp.TP_BF16, tp.TP_ATTN), tp.TP_OK),             # d = 128: fused, no s x s
+    ((768, 16, 47104, 1, 1, 0, tp.TP_BF16, tp.TP_ATTN), tp.TP_EUNSUPPORTED),   # d = 48: materialised
 ])
 def test_check_args(args, expect):
     assert tp.tp_check_args(*args) == expect
@@ -122,6 +134,16 @@ def test_reduce_and_gemm_validation_on_host():
     assert L.tp_reduce_partials(tp.TP_BF16, 4, 16, 2, a, _fake(0x100008), none, a, None) == tp.TP_EALIGN
     assert L.tp_gemm(tp.TP_BF16, 20, 16, 16, 1.0, a, 16, 1, a, 16, 1, None, a, 16, None, 0, None) == tp.TP_EUNSUPPORTED
     assert L.tp_gemm(tp.TP_BF16, 16, 16, 32, 1.0, a, 16, 1, a, 32, 1, None, a, 16, None, 0, None) == tp.TP_EINVAL
+    # operands and output below 2^31 elements: rows x leading dimension
+    big = 1 << 16
+    assert L.tp_gemm(tp.TP_BF16, big, 64, 32768, 1.0, a, 32768, 1, a, 64, 0, None, a, 64, None, 0,
+                     None) == tp.TP_EUNSUPPORTED                                  # A [65536, 32768]
+    assert L.tp_gemm(tp.TP_BF16, 64, big, 32768, 1.0, a, 32768, 1, a, 32768, 1, None, a, big, None, 0,
+                     None) == tp.TP_EUNSUPPORTED                                  # B [65536, 32768]
+    assert L.tp_gemm(tp.TP_BF16, 64, 64, big, 1.0, a, 32768, 0, a, 64, 0, None, a, 64, None, 0,
+                     None) == tp.TP_EUNSUPPORTED                                  # A stored [K=65536, 32768]
+    assert L.tp_gemm(tp.TP_BF16, big, 32768, 64, 1.0, a, 64, 1, a, 32768, 0, None, a, 32768, None, 0,
+                     None) == tp.TP_EUNSUPPORTED                                  # C [65536, 32768]
     # stream-K over the partial wave behind a whole one needs fp32 fragment slots (384 tiles: 128 tiles in
     # 2 pieces each): workspace checked before any launch
     M, N, K = 2048, 12288, 6144
