@@ -63,7 +63,8 @@ enum tp_status {
   TP_ENULL = -3,         /* a required pointer is NULL */
   TP_EALIGN = -4,        /* a pointer is not 16-byte aligned */
   TP_EWORKSPACE = -5,    /* workspace_bytes < tp_workspace_bytes(...) */
-  TP_EHIP = -6           /* a HIP launch failed */
+  TP_EHIP = -6,          /* a HIP launch failed */
+  TP_ESCRATCH = -7       /* tp_layer_bwd_noalloc: the call needs more than tp_noalloc_scratch_bytes() */
 };
 
 /* Rank-local weights of one block.
@@ -148,6 +149,23 @@ int tp_layer_bwd(int h, int a, int s, int b, int t, int rank, int dtype, int blo
                  const void *x, const tp_block_weights *w, const void *saved, const void *dy,
                  void *dx_partial, const tp_block_grads *g,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* tp_layer_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The workspace is a buffer the
+ * library holds in device memory (a file-scope array of
+ * tp_noalloc_scratch_bytes() = 256 MiB, one copy on each GPU it runs on,
+ * kept until the process ends); the call allocates and frees nothing.
+ * Arguments, results and errors as tp_layer_bwd, plus TP_ESCRATCH when
+ * tp_workspace_bytes(h, a, s, b, t, dtype, block) exceeds the buffer (e.g.
+ * the attention block of h=2304, a=24, s=2048, b=4, t=1 needs 289 MiB).
+ * Every call on one GPU shares that GPU's buffer: calls that overlap in time
+ * on one GPU (different streams or threads without ordering) race and give
+ * wrong results. Calls in order on one stream are safe.                    */
+size_t tp_noalloc_scratch_bytes(void);
+int tp_layer_bwd_noalloc(int h, int a, int s, int b, int t, int rank, int dtype, int block,
+                         const void *x, const tp_block_weights *w, const void *saved, const void *dy,
+                         void *dx_partial, const tp_block_grads *g, void *stream);
 
 /* Stand-in for the all-reduce on one GPU, fused with the bias + residual add
  * that follows it:

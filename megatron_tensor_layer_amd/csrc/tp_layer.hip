@@ -35,7 +35,7 @@
 #include <type_traits>
 #include <vector>
 
-#include "../../include/tp_layer.h"
+#include "tp_layer.h"
 #include "aux_kernels.hpp"
 #include "gemm.hpp"
 #include "flash_attn.hpp"
@@ -80,6 +80,10 @@ struct Rec {
   double flops, bytes;
 };
 std::atomic<bool> on{false};
+// set for the duration of a tp_layer_bwd_noalloc call: no events are created
+// or recorded, so that call makes no allocating runtime call even while
+// profiling is on
+thread_local bool suppressed = false;
 std::mutex mu;
 std::vector<Rec> recs;
 std::vector<hipEvent_t> pool;
@@ -106,7 +110,7 @@ struct Scope {
   hipStream_t st;
   hipEvent_t a = nullptr;
   Scope(int r, double f, double by, hipStream_t s) : role(r), flops(f), bytes(by), st(s) {
-    if (on.load(std::memory_order_relaxed)) {
+    if (on.load(std::memory_order_relaxed) && !suppressed) {
       a = take();
       if (a) (void)hipEventRecord(a, st);
     }
@@ -1129,6 +1133,43 @@ int ln_check(int dtype, long rows, long h) {
   return TP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// library-owned scratch for callers that cannot allocate (tp_layer_bwd_noalloc)
+// ---------------------------------------------------------------------------
+
+// Each GPU that runs the library holds its own copy of this array until the
+// process ends. In host code `scratch` names a host-side stand-in: kernels
+// and copies take the device address from scratch_ptr() instead.
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return TP_EINVAL;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return TP_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return TP_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1184,6 +1225,25 @@ int tp_layer_bwd(int h, int a, int s, int b, int t, int rank, int dtype, int blo
   hipStream_t st = static_cast<hipStream_t>(stream);
   return block == TP_ATTN ? attn_bwd(D, x, w, saved, dy, dx_partial, g, workspace, st)
                           : mlp_bwd(D, x, w, saved, dy, dx_partial, g, workspace, st);
+}
+
+size_t tp_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int tp_layer_bwd_noalloc(int h, int a, int s, int b, int t, int rank, int dtype, int block, const void* x,
+                         const tp_block_weights* w, const void* saved, const void* dy, void* dx_partial,
+                         const tp_block_grads* g, void* stream) {
+  int rc = check_args(h, a, s, b, t, rank, dtype, block);
+  if (rc != TP_OK) return rc;
+  if (ws_layout(make_dims(h, a, s, b, t, dtype), block).total > kScratchBytes) return TP_ESCRATCH;
+  void* ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc != TP_OK) return rc;
+  // same checks and kernels as tp_layer_bwd, on the library's scratch (no
+  // kernel relies on the scratch's contents at entry, so nothing is cleared)
+  prof::suppressed = true;
+  rc = tp_layer_bwd(h, a, s, b, t, rank, dtype, block, x, w, saved, dy, dx_partial, g, ws, kScratchBytes, stream);
+  prof::suppressed = false;
+  return rc;
 }
 
 int tp_reduce_partials(int dtype, long rows, long cols, int t, const void* partials, const void* bias,
@@ -1371,6 +1431,7 @@ const char* tp_strerror(int code) {
     case TP_ENULL: return "a required pointer is NULL";
     case TP_EALIGN: return "a pointer is not 16-byte aligned";
     case TP_EWORKSPACE: return "workspace smaller than tp_workspace_bytes()";
+    case TP_ESCRATCH: return "the call needs more scratch than the library's static buffer (tp_noalloc_scratch_bytes())";
     case TP_EHIP: return g_hip_err[0] ? g_hip_err : "HIP error";
   }
   return "unknown error code";

@@ -19,13 +19,15 @@ TP_ATTN, TP_MLP = 0, 1
 
 TP_OK = 0
 TP_EINVAL, TP_EUNSUPPORTED, TP_ENULL, TP_EALIGN, TP_EWORKSPACE, TP_EHIP = -1, -2, -3, -4, -5, -6
+TP_ESCRATCH = -7
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtplayer.so")
 
 # every symbol include/tp_layer.h declares
 EXPORTS = ("tp_check_args", "tp_saved_bytes", "tp_workspace_bytes", "tp_layer_fwd", "tp_layer_bwd",
            "tp_reduce_partials", "tp_layer_bwd_recompute", "tp_layernorm_fwd", "tp_layernorm_bwd",
-           "tp_gemm_workspace_bytes", "tp_gemm", "tp_prof_enable", "tp_prof_read", "tp_strerror")
+           "tp_gemm_workspace_bytes", "tp_gemm", "tp_prof_enable", "tp_prof_read", "tp_strerror",
+           "tp_noalloc_scratch_bytes", "tp_layer_bwd_noalloc")
 
 _lib = None
 
@@ -69,6 +71,10 @@ def lib():
     L.tp_layer_bwd.argtypes = dims + [vp, ctypes.POINTER(TPBlockWeights), vp, vp, vp,
                                       ctypes.POINTER(TPBlockGrads), vp, sz, vp]
     L.tp_layer_bwd.restype = i
+    L.tp_noalloc_scratch_bytes.argtypes, L.tp_noalloc_scratch_bytes.restype = [], sz
+    L.tp_layer_bwd_noalloc.argtypes = dims + [vp, ctypes.POINTER(TPBlockWeights), vp, vp, vp,
+                                              ctypes.POINTER(TPBlockGrads), vp]
+    L.tp_layer_bwd_noalloc.restype = i
     L.tp_reduce_partials.argtypes = [i, lng, lng, i, vp, vp, vp, vp, vp]
     L.tp_reduce_partials.restype = i
     L.tp_layer_bwd_recompute.argtypes = dims + [vp, ctypes.POINTER(TPBlockWeights), vp, vp,
@@ -177,6 +183,29 @@ def tp_layer_bwd(h, a, s, b, t, rank, dtype, block, x, w, saved, dy, dx_partial,
                             _ptr(dx_partial), ctypes.byref(G), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "tp_layer_bwd")
+
+
+def tp_noalloc_scratch_bytes():
+    return int(lib().tp_noalloc_scratch_bytes())
+
+
+def tp_layer_bwd_noalloc(h, a, s, b, t, rank, dtype, block, x, w, saved, dy, dx_partial, g, stream=None):
+    """tp_layer_bwd on the library's own device scratch (no workspace argument)."""
+    dt = torch_dtype(dtype)
+    T = s * b
+    shapes = block_shapes(h, t, block)
+    for name, tens, shp in zip(("w_in", "b_in", "w_out", "b_out"), w, shapes):
+        _expect(tens, int(torch.Size(shp).numel()), dt, name)
+    for name, tens, shp in zip(("dw_in", "db_in", "dw_out", "db_out"), g, shapes):
+        _expect(tens, int(torch.Size(shp).numel()), dt, name)
+    _expect(x, T * h, dt, "x")
+    _expect(dy, T * h, dt, "dy")
+    _expect(dx_partial, T * h, dt, "dx_partial")
+    W = TPBlockWeights(*[t_.data_ptr() for t_ in w])
+    G = TPBlockGrads(*[t_.data_ptr() for t_ in g])
+    rc = lib().tp_layer_bwd_noalloc(h, a, s, b, t, rank, dtype, block, _ptr(x), ctypes.byref(W), _ptr(saved),
+                                    _ptr(dy), _ptr(dx_partial), ctypes.byref(G), _stream(stream))
+    _check(rc, "tp_layer_bwd_noalloc")
 
 
 def tp_reduce_partials(dtype, partials, out, bias=None, residual=None, stream=None):

@@ -165,8 +165,30 @@ def test_profiler_without_gpu_work():
     tp.tp_prof_enable(False)
 
 
+def test_noalloc_validation_on_host():
+    """tp_layer_bwd_noalloc checks its arguments and the scratch it needs
+    before any HIP call."""
+    L = tp.lib()
+    assert tp.tp_noalloc_scratch_bytes() == 256 << 20
+    W = tp.TPBlockWeights(0x10000, 0x20000, 0x30000, 0x40000)
+    G = tp.TPBlockGrads(0x50000, 0x60000, 0x70000, 0x80000)
+    a = _fake(0x100000)
+    # invalid dims first
+    assert L.tp_layer_bwd_noalloc(64, 4, 32, 2, 3, 0, tp.TP_FP32, tp.TP_ATTN, a, ctypes.byref(W), a, a, a,
+                                  ctypes.byref(G), None) == tp.TP_EINVAL
+    # the 1.7B attention block needs more workspace than the static scratch holds
+    assert tp.tp_workspace_bytes(2304, 24, 2048, 4, 1, tp.TP_BF16, tp.TP_ATTN) > tp.tp_noalloc_scratch_bytes()
+    assert L.tp_layer_bwd_noalloc(2304, 24, 2048, 4, 1, 0, tp.TP_BF16, tp.TP_ATTN, a, ctypes.byref(W), a, a, a,
+                                  ctypes.byref(G), None) == tp.TP_ESCRATCH
+    # every benchmark shape of the 175B, 18B and 1T layers fits
+    for h, a_, s, b, t in ((12288, 96, 2048, 1, 8), (6144, 48, 2048, 2, 8), (25600, 160, 2048, 1, 8)):
+        for blk in (tp.TP_ATTN, tp.TP_MLP):
+            assert tp.tp_workspace_bytes(h, a_, s, b, t, tp.TP_BF16, blk) <= tp.tp_noalloc_scratch_bytes()
+
+
 def test_strerror():
-    for code in (tp.TP_OK, tp.TP_EINVAL, tp.TP_EUNSUPPORTED, tp.TP_ENULL, tp.TP_EALIGN, tp.TP_EWORKSPACE, tp.TP_EHIP):
+    for code in (tp.TP_OK, tp.TP_EINVAL, tp.TP_EUNSUPPORTED, tp.TP_ENULL, tp.TP_EALIGN, tp.TP_EWORKSPACE, tp.TP_EHIP,
+                 tp.TP_ESCRATCH):
         assert len(tp.strerror(code)) > 0
     assert "unknown" in tp.strerror(-99)
 
