@@ -81,6 +81,7 @@ struct GemmArgs {
   const float* rowv; long r_s1, r_s2;
   float alpha;
   float* part;
+  void* csum;  // direct bf16 kernel, grouped launches: bf16 [N] sum over k of B[k, n] (tiles of tile-row 0)
 };
 
 // Stream-K launch plan (direct bf16 kernel, batch 1). Blocks [0, dp_tiles)

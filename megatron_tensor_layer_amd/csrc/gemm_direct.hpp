@@ -63,6 +63,18 @@ __device__ __forceinline__ uint2 read_tr(const uint4* lds, uint32_t byte_off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPL_LDS v4i16_t*)p));
 }
 
+// Sum of the 8 bf16 of a fragment, added to acc: v_dot2_f32_bf16 against
+// (1, 1), one instruction per dword, in a fixed order.
+__device__ __forceinline__ float colsum8(const uint4& f, float acc) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 one = __builtin_bit_cast(bf2, 0x3f803f80u);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, f.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, f.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, f.z), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, f.w), one, acc, false);
+  return acc;
+}
+
 // One operand's tile loader + fragment reader. R = rows of the operand tile
 // along M (or N); KMAJ = operand stored K-contiguous in HBM.
 // XOR swizzle of the 16-byte chunks of K-contiguous LDS row `row`: distinct for
@@ -149,7 +161,15 @@ struct DirectOperand {
 // piece `split`, batch z. LDS buffers are passed in (two per operand).
 // EPI_SK_PART: K range [kb_, ke_) and the fp32 fragment goes to skdst as a
 // row-major BM x BN tile.
-template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int KSEG>
+// CSUM: the tile also sums its B operand over its whole K range, column by
+// column (p.csum[n] = sum over k of B[k, n], rounded once to bf16): a bias
+// gradient is the column sum of the weight-gradient GEMM's right operand
+// (db = sum over tokens of dY, with dW = X^T dY), so the tiles of tile-row 0
+// produce it from the B fragments they already hold. Each lane holds 8
+// consecutive k of one column per fragment and adds them with two-element
+// bf16 dot products against (1, 1) in a fixed order; lanes l and l + 32
+// hold the two k halves of a column and are added at the end.
+template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int KSEG, bool CSUM = false>
 __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split, int z, uint4* sa0, uint4* sb0,
                                             uint4* sa1, uint4* sb1, int kb_ = 0, int ke_ = 0,
                                             float* skdst = nullptr) {
@@ -252,12 +272,18 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   };
   constexpr int NLD = OA::PER_WAVE + OB::PER_WAVE;  // global->LDS loads per tile and wave
   constexpr int NR = TM + TN, DPS = (NLD + 1) / 2;
+  float cs[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) cs[j] = 0.0f;
   auto slot_step = [&](int set_mma, const uint4* Ar, const uint4* Br, int ks_rd, int set_rd, int dq0,
                        const bf16_t* na, const bf16_t* nb, uint4* la, uint4* lb) {
 #pragma unroll
     for (int q = 0; q < MF; ++q) {
       const int j = q / TM, i = q - (q / TM) * TM;
       mma16(bq[set_mma][j], af[set_mma][i], acc[i][j], bf16_t{});
+      if constexpr (CSUM) {
+        if (i == 0) cs[j] = colsum8(bq[set_mma][j], cs[j]);
+      }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         if ((r * MF) / NR == q) {
@@ -312,6 +338,17 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   }
   wait_loads();
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (CSUM) {
+    // waves of the first wave-row hold every column of the tile once
+    if (wm == 0 && tm == 0) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const float v = cs[j] + __shfl_xor(cs[j], 32);
+        const int col = n0 + wn * WTN + j * 32 + lane;
+        if (lane < 32 && col < p.N) static_cast<bf16_t*>(p.csum)[col] = f2bf(v);
+      }
+    }
+  }
 
   // Epilogue through LDS. Stored straight from the MFMA layout, a lane holds
   // 4 columns of one row and a store instruction touches 32 rows, which
@@ -461,8 +498,13 @@ gemm_pair_kernel(const GemmArgs p0, const GemmArgs p1, int tiles0, int units0, i
     direct_tile<Cfg, K0::AK, K0::BK, K0::EPI, typename K0::TO, 1>(p0, u - split * tiles0, split, 0, sa0,
                                                                                  sb0, sa1, sb1);
   } else {
-    direct_tile<Cfg, K1::AK, K1::BK, K1::EPI, typename K1::TO, 1>(p1, u - units0, 0, 0, sa0, sb0, sa1,
-                                                                                 sb1);
+    const int L = u - units0;
+    int tm, tn;
+    tile_coords(p1, tm, tn, L);
+    if (p1.csum && tm == 0)
+      direct_tile<Cfg, K1::AK, K1::BK, K1::EPI, typename K1::TO, 1, true>(p1, L, 0, 0, sa0, sb0, sa1, sb1);
+    else
+      direct_tile<Cfg, K1::AK, K1::BK, K1::EPI, typename K1::TO, 1>(p1, L, 0, 0, sa0, sb0, sa1, sb1);
   }
 }
 

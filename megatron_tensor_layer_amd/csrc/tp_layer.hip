@@ -641,9 +641,14 @@ struct RowdotFuse {
   float* D;        // [b, a_r, s]
 };
 
+// csum (bf16 [N1], may be NULL): the column sums of problem 1's B operand
+// (the bias gradient), formed inside the grouped launch by the tiles of
+// tile-row 0; *csum_done tells whether that happened (else the caller runs
+// the column-sum kernel).
 template <int E0, int ROLE, int ROLE0, int ROLE1>
 hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_t st,
-                const RowdotFuse* rd = nullptr, bool* rd_done = nullptr) {
+                const RowdotFuse* rd = nullptr, bool* rd_done = nullptr, void* csum = nullptr,
+                bool* csum_done = nullptr) {
   using K0 = GemmKind<true, true, E0, bf16_t>;
   using K1 = GemmKind<false, false, EPI_LINEAR, bf16_t>;
   const bool direct = D.dt == TP_BF16 && direct_ok<CfgBig>(p0, 1) && direct_ok<CfgBig>(p1, 1);
@@ -673,6 +678,8 @@ hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_
   }
   const int units0 = tiles0 * splits;
   const int first1 = p1.K > P.chunk ? 1 : 0;
+  p1.csum = csum;
+  if (csum_done) *csum_done = csum != nullptr;
   if (splits > 1) {
     hipLaunchKernelGGL((gemm_pair_kernel<CfgBig, GemmKind<true, true, EPI_PARTIAL, float>, K1, ROLE>),
                        dim3(units0 + tiles1), dim3(CfgBig::NT), 0, st, p0, p1, tiles0, units0, tiles1, first1);
@@ -925,10 +932,13 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     q.B = dy; q.ldb = D.h;
     q.C = g->dw_out; q.ldc = D.h;
     // (a split-K dC also gives D = rowsum(dC * C) in its summing pass)
+    // (and dbo = sum over tokens of dH, a replica, from the weight-gradient
+    // tiles' dH fragments)
     const RowdotFuse rdf{C32, Dv};
-    TRY((pair<EPI_LINEAR, R_O_BWD, R_O_DGRAD, R_O_WGRAD>(D, p, q, part, st, &rdf, &rd_done)));
+    bool cs_done = false;
+    TRY((pair<EPI_LINEAR, R_O_BWD, R_O_DGRAD, R_O_WGRAD>(D, p, q, part, st, &rdf, &rd_done, g->db_out, &cs_done)));
+    if (!cs_done) TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, st));
   }
-  TRY(colsum<R_DBO>(D, dy, g->db_out, D.T, D.h, D.h, st));  // dbo (replica)
   if (!rd_done) {  // D = rowsum(dC * C) per (sequence, head, query)
     prof::Scope sc(R_ROWDOT, 2.0 * D.T * D.hr, D.T * D.hr * (es + 4.0) + 4.0 * D.z * D.s, st);
     if (D.dt == TP_BF16) TRY(rowdot_t<bf16_t>(D, dC, C32, Dv, st));
@@ -1006,9 +1016,12 @@ int attn_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void
     q.A = x; q.lda = D.h;
     q.B = dqkv; q.ldb = D.q3;
     q.C = g->dw_in; q.ldc = D.q3;
-    TRY((pair<EPI_LINEAR, R_QKV_BWD, R_QKV_DGRAD, R_QKV_WGRAD>(D, p, q, part, st)));
+    // db_qkv = sum over tokens of dQKV
+    bool cs_done = false;
+    TRY((pair<EPI_LINEAR, R_QKV_BWD, R_QKV_DGRAD, R_QKV_WGRAD>(D, p, q, part, st, nullptr, nullptr, g->db_in,
+                                                               &cs_done)));
+    if (!cs_done) TRY(colsum<R_DBQKV>(D, dqkv, g->db_in, D.T, D.q3, D.q3, st));
   }
-  TRY(colsum<R_DBQKV>(D, dqkv, g->db_in, D.T, D.q3, D.q3, st));
   return TP_OK;
 }
 
@@ -1060,9 +1073,12 @@ int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void*
     q.A = Z; q.lda = D.fr;
     q.B = dy; q.ldb = D.h;
     q.C = g->dw_out; q.ldc = D.h;
-    TRY((pair<EPI_GELU_BWD, R_FC2_BWD, R_FC2_DGRAD, R_FC2_WGRAD>(D, p, q, part, st)));
+    // db2 = sum over tokens of dY (a replica)
+    bool cs_done = false;
+    TRY((pair<EPI_GELU_BWD, R_FC2_BWD, R_FC2_DGRAD, R_FC2_WGRAD>(D, p, q, part, st, nullptr, nullptr, g->db_out,
+                                                                 &cs_done)));
+    if (!cs_done) TRY(colsum<R_DB2>(D, dy, g->db_out, D.T, D.h, D.h, st));
   }
-  TRY(colsum<R_DB2>(D, dy, g->db_out, D.T, D.h, D.h, st));  // db2 (replica)
   {  // dH_r = dU W1_r^T
     GemmArgs p = gargs(D.T, D.h, D.fr);
     p.A = dU; p.lda = D.fr;
@@ -1073,9 +1089,12 @@ int mlp_bwd(const Dims& D, const void* x, const tp_block_weights* w, const void*
     q.A = x; q.lda = D.h;
     q.B = dU; q.ldb = D.fr;
     q.C = g->dw_in; q.ldc = D.fr;
-    TRY((pair<EPI_LINEAR, R_FC1_BWD, R_FC1_DGRAD, R_FC1_WGRAD>(D, p, q, part, st)));
+    // db1 = sum over tokens of dU
+    bool cs_done = false;
+    TRY((pair<EPI_LINEAR, R_FC1_BWD, R_FC1_DGRAD, R_FC1_WGRAD>(D, p, q, part, st, nullptr, nullptr, g->db_in,
+                                                               &cs_done)));
+    if (!cs_done) TRY(colsum<R_DB1>(D, dU, g->db_in, D.T, D.fr, D.fr, st));
   }
-  TRY(colsum<R_DB1>(D, dU, g->db_in, D.T, D.fr, D.fr, st));
   return TP_OK;
 }
 

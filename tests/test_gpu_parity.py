@@ -342,16 +342,22 @@ def test_profiler_attributes_every_role(name):
     full_layer_gpu(cfg)
     tp.tp_prof_enable(False)
     prof = tp.tp_prof_read()
-    roles = {"qkv_fwd", "o_fwd", "fc1_fwd", "fc2_fwd", "db2", "db1", "dbo", "rowdot", "dbqkv", "reduce"}
+    roles = {"qkv_fwd", "o_fwd", "fc1_fwd", "fc2_fwd", "rowdot", "reduce"}
     roles |= attention_roles(cfg)
     # the fused and the materialised attention never both run
     other = {"attn_fwd", "attn_dkv", "attn_dq", "scores", "softmax", "pv", "ds", "dv", "dq", "dk"} - roles
     assert not (other & set(prof)), other & set(prof)
     # a weight's input- and weight-gradient GEMMs run as one grouped launch
-    # when both take whole 64-deep K steps, else as two launches
-    for w in ("fc2", "fc1", "o", "qkv"):
+    # when both take whole 64-deep K steps, else as two launches; the grouped
+    # launch also forms the bias gradient (column sums of its weight-gradient
+    # operand), else a column-sum kernel does
+    for w, db in (("fc2", "db2"), ("fc1", "db1"), ("o", "dbo"), ("qkv", "dbqkv")):
         grouped = f"{w}_dgrad+wgrad"
-        roles |= {grouped} if grouped in prof else {f"{w}_dgrad", f"{w}_wgrad"}
+        if grouped in prof:
+            roles |= {grouped}
+            assert db not in prof, db
+        else:
+            roles |= {f"{w}_dgrad", f"{w}_wgrad", db}
     assert roles <= set(prof)
     for name in roles - {"reduce"}:
         assert prof[name]["launches"] == cfg.t, name
