@@ -21,15 +21,14 @@
 // three MFMA passes keep about 16 mantissa bits of the logits, which the
 // peaked softmax rows of wide layers need.
 //
-// Kernels (4 waves of 64 lanes):
-//   fa_fwd_kernel    : 128 queries (32 per wave); keys in tiles of 64 staged
-//                      in LDS (Kh, Kl, V; double buffered); writes C (bf16 and
-//                      fp32) and the log2-domain log-sum-exp. fa_fwd2_kernel is
-//                      the same with single-buffered tiles: within 256
-//                      registers per lane and 48 KB of LDS (d <= 128), two
-//                      workgroups share a CU and one computes while the other
-//                      waits for its tile (the scores' VALU work and the MFMAs
-//                      of one wave cannot overlap much on their own).
+// Kernels (64-lane waves of 32 query or key rows each):
+//   fa_fwd8_kernel   : 256 queries, 8 waves (d <= 128): keys in tiles of 64
+//                      staged in LDS (Kh, Kl, V; double buffered, 96 KB at
+//                      d = 128); two waves share each SIMD, so one wave's
+//                      softmax arithmetic and waits overlap the other's MFMAs;
+//                      writes C (bf16 and fp32) and the log2-domain
+//                      log-sum-exp. fa_fwd_kernel: the same with 4 waves and
+//                      128 queries, for d = 160 (more live state per wave).
 //   fa_bwd_dkv_kernel: 128 keys (32 per wave); queries in tiles of 64 (Qh,
 //                      Ql, dC + LSE and D); accumulates dK, dV.
 //   fa_bwd_dq_kernel : 128 queries; keys in tiles of 64; dQ (fa_bwd_dq2_kernel:
@@ -94,7 +93,8 @@ struct FaArgs {
 
 namespace fa {
 
-constexpr int BQ = 128;  // queries (fwd, dq) or keys (dkv) per block: 4 waves x 32
+constexpr int BQ = 128;  // queries (dq) or keys (dkv) per block: 4 waves x 32
+constexpr int BQF = 256; // queries per block of the forward kernel with 8 waves (d <= 128)
 constexpr int BT = 64;   // rows per staged LDS tile
 
 __host__ __device__ inline int asw(int r) { return ((r & 2) << 1) | ((r >> 2) & 3); }
@@ -104,20 +104,20 @@ __host__ __device__ inline int asw(int r) { return ((r & 2) << 1) | ((r >> 2) & 
 struct Item {
   int blk, c, nch, t0, t1;  // block, chunk, chunks of the block, tile range [t0, t1)
 };
-// Tile range of a block: keys [0, end of its queries) for query blocks,
-// queries [its first key, s) for key blocks.
-__host__ __device__ inline void block_range(int blk, int s, bool keyblocks, int& t0, int& t1) {
-  const int ntot = (s + BT - 1) / BT, qe = (blk + 1) * BQ < s ? (blk + 1) * BQ : s;
-  t0 = keyblocks ? 2 * blk : 0;
+// Tile range of a block of bq rows: keys [0, end of its queries) for query
+// blocks, queries [its first key, s) for key blocks.
+__host__ __device__ inline void block_range(int blk, int s, bool keyblocks, int& t0, int& t1, int bq = BQ) {
+  const int ntot = (s + BT - 1) / BT, qe = (blk + 1) * bq < s ? (blk + 1) * bq : s;
+  t0 = keyblocks ? blk * (bq / BT) : 0;
   t1 = keyblocks ? ntot : (qe + BT - 1) / BT;
 }
 // Item idx of one head: blocks heaviest first, each cut into chunks.
-__host__ __device__ inline Item item_of(int idx, int s, int ct, bool keyblocks) {
-  const int nblk = (s + BQ - 1) / BQ;
+__host__ __device__ inline Item item_of(int idx, int s, int ct, bool keyblocks, int bq = BQ) {
+  const int nblk = (s + bq - 1) / bq;
   for (int j = 0; j < nblk; ++j) {
     const int blk = keyblocks ? j : nblk - 1 - j;
     int t0, t1;
-    block_range(blk, s, keyblocks, t0, t1);
+    block_range(blk, s, keyblocks, t0, t1, bq);
     const int nch = (t1 - t0 + ct - 1) / ct;
     if (idx < nch) {
       const int e = t0 + (idx + 1) * ct;
@@ -127,12 +127,12 @@ __host__ __device__ inline Item item_of(int idx, int s, int ct, bool keyblocks) 
   }
   return {-1, 0, 0, 0, 0};
 }
-__host__ __device__ inline int items_per_head(int s, int ct, bool keyblocks) {
-  const int nblk = (s + BQ - 1) / BQ;
+__host__ __device__ inline int items_per_head(int s, int ct, bool keyblocks, int bq = BQ) {
+  const int nblk = (s + bq - 1) / bq;
   int n = 0;
   for (int blk = 0; blk < nblk; ++blk) {
     int t0, t1;
-    block_range(blk, s, keyblocks, t0, t1);
+    block_range(blk, s, keyblocks, t0, t1, bq);
     n += (t1 - t0 + ct - 1) / ct;
   }
   return n;
@@ -146,10 +146,10 @@ __device__ __forceinline__ void xcd_item(int L, int zs, int items, int& z, int& 
   z = i / items;
   idx = i - z * items;
 }
-// fp32 slot of (z, block, chunk): 128 rows x d per accumulated matrix
-__host__ __device__ inline long part_slot(int z, int blk, int c, int s, int ct, int d) {
-  const int nblk = (s + BQ - 1) / BQ, ncmax = ((s + BT - 1) / BT + ct - 1) / ct;
-  return (((long)z * nblk + blk) * ncmax + c) * (long)BQ * d;
+// fp32 slot of (z, block, chunk): bq rows x d per accumulated matrix
+__host__ __device__ inline long part_slot(int z, int blk, int c, int s, int ct, int d, int bq = BQ) {
+  const int nblk = (s + bq - 1) / bq, ncmax = ((s + BT - 1) / BT + ct - 1) / ct;
+  return (((long)z * nblk + blk) * ncmax + c) * (long)bq * d;
 }
 
 // ---- LDS tiles ----------------------------------------------------------------
@@ -160,12 +160,13 @@ __host__ __device__ inline long part_slot(int z, int blk, int c, int s, int ct, 
 // crosses the sequence end repeats its last valid row, and columns >= d
 // repeat column 0: in bounds, and only ever multiplied into outputs that are
 // masked or never stored.
-template <int DP>
+template <int DP, int NW = 4>
 struct Tile {
   static constexpr int PANELS = DP / 64;
   static constexpr int BYTES = PANELS * 8192;
-  static constexpr int U4 = BYTES / 16;        // uint4 per tile
-  static constexpr int PER_WAVE = PANELS * 2;  // loads per wave (4 waves)
+  static constexpr int U4 = BYTES / 16;             // uint4 per tile
+  static constexpr int PER_WAVE = PANELS * 8 / NW;  // loads per wave (NW waves)
+  static_assert(PER_WAVE * NW == PANELS * 8, "the tile's loads split evenly over the waves");
   uint32_t off[PER_WAVE];
   __device__ __forceinline__ void init(int rows, long ld, int d, int wave, int lane) {
 #pragma unroll
@@ -419,20 +420,22 @@ __device__ __forceinline__ void rows_store(bf16_t* dst, float* dst32, const f32x
 // forward: 1-D grid of z * items workgroups; one item = one chunk of key
 // tiles of a block of 128 queries
 // ---------------------------------------------------------------------------
-// NBUF = 2: one workgroup per CU, the next key tile loads while this one is
-// computed. NBUF = 1: single-buffered tiles (48 KB of LDS at d = 128) so that
-// two workgroups share a CU and each computes while the other waits.
-template <int D, int NBUF>
+// NW waves of 32 queries each: a block is 32 NW queries; one workgroup per
+// CU, the next key tile loads while this one is computed (double-buffered).
+// With NW = 8 two waves share each SIMD, so one's softmax arithmetic and
+// waits overlap the other's MFMAs, and every staged key tile serves 256
+// queries.
+template <int D, int NW>
 __device__ __forceinline__ void fa_fwd_body(const FaArgs& a, uint4* lds) {
-  constexpr int DP = (D + 63) / 64 * 64, KS = D / 16, NB = D / 32;
-  using TL = fa::Tile<DP>;
+  constexpr int DP = (D + 63) / 64 * 64, KS = D / 16, NB = D / 32, BQW = 32 * NW;
+  using TL = fa::Tile<DP, NW>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int z, idx;
   fa::xcd_item(blockIdx.x, a.z, a.items, z, idx);
   const int beta = z / a.ar, head = z - (z / a.ar) * a.ar;
-  const fa::Item it = fa::item_of(idx, a.s, a.ct, false);
-  const int q0 = it.blk * fa::BQ;
+  const fa::Item it = fa::item_of(idx, a.s, a.ct, false, BQW);
+  const int q0 = it.blk * BQW;
   const long ld = (long)a.b * a.q3, ldl = (long)a.b * 2 * a.hr;
   const bf16_t* Qh = a.qkv + (long)beta * a.q3 + head * a.d;
   const bf16_t* Kh = Qh + a.hr;
@@ -455,7 +458,7 @@ __device__ __forceinline__ void fa_fwd_body(const FaArgs& a, uint4* lds) {
   f32x16_t o[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) fa::zero(o[nb]);
-  float m = -INFINITY, l = 0.0f;  // every row sees its chunk's first key (chunks start at multiples of 128)
+  float m = -INFINITY, l = 0.0f;  // every row sees its chunk's first key (chunks start at multiples of BQW)
   // key tiles this wave's rows can see (none if all its rows are past s)
   const int wt = q0 + 32 * wave < a.s ? min(it.t1, cdiv(min(a.s, q0 + 32 * wave + 32), fa::BT)) : 0;
 
@@ -530,29 +533,19 @@ __device__ __forceinline__ void fa_fwd_body(const FaArgs& a, uint4* lds) {
     wait_loads();
     __syncthreads();
   };
-  if constexpr (NBUF == 2) {
-    issue(it.t0, 0);
-    wait_loads();
-    __syncthreads();
-    for (int t = it.t0; t < it.t1; t += 2) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 < it.t1) step(std::integral_constant<int, 1>{}, t + 1);
-    }
-  } else {
-    for (int t = it.t0; t < it.t1; ++t) {
-      issue(t, 0);
-      wait_loads();
-      __syncthreads();
-      compute(std::integral_constant<int, 0>{}, t);
-      __syncthreads();
-    }
+  issue(it.t0, 0);
+  wait_loads();
+  __syncthreads();
+  for (int t = it.t0; t < it.t1; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < it.t1) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   if (it.nch > 1) {  // partial: unnormalised C, running maximum and sum
-    fa::part_store<NB>(a.part + fa::part_slot(z, it.blk, it.c, a.s, a.ct, D), o, wave, lane);
+    fa::part_store<NB>(a.part + fa::part_slot(z, it.blk, it.c, a.s, a.ct, D, BQW), o, wave, lane);
     if (g == 0) {
-      float2* ml = reinterpret_cast<float2*>(a.part + fa::part_slot(a.z, 0, 0, a.s, a.ct, D));
-      ml[fa::part_slot(z, it.blk, it.c, a.s, a.ct, 1) + 32 * wave + r32] = make_float2(m, l);
+      float2* ml = reinterpret_cast<float2*>(a.part + fa::part_slot(a.z, 0, 0, a.s, a.ct, D, BQW));
+      ml[fa::part_slot(z, it.blk, it.c, a.s, a.ct, 1, BQW) + 32 * wave + r32] = make_float2(m, l);
     }
   } else if (qrow < a.s) {
     const long trow = (long)qrow * a.b + beta;
@@ -561,45 +554,49 @@ __device__ __forceinline__ void fa_fwd_body(const FaArgs& a, uint4* lds) {
   }
 }
 
+// 4 waves, 128-query blocks (d = 160: more live state than two waves per
+// SIMD can hold)
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) fa_fwd_kernel(const FaArgs a) {
   __shared__ __attribute__((aligned(1024))) uint4 lds[2 * 3 * fa::Tile<(D + 63) / 64 * 64>::U4];
-  fa_fwd_body<D, 2>(a, lds);
+  fa_fwd_body<D, 4>(a, lds);
 }
+// 8 waves, 256-query blocks (d <= 128)
 template <int D>
-__global__ void __launch_bounds__(256, 2) fa_fwd2_kernel(const FaArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint4 lds[3 * fa::Tile<(D + 63) / 64 * 64>::U4];
-  fa_fwd_body<D, 1>(a, lds);
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) fa_fwd8_kernel(const FaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint4 lds[2 * 3 * fa::Tile<(D + 63) / 64 * 64>::U4];
+  fa_fwd_body<D, 8>(a, lds);
 }
 
-// Forward combine: grid (blocks * D / 8, z), one float4 of a block's
-// 128 x D context per thread, in the partials' register order. For a query
+// Forward combine: grid (blocks * NW * D / 32, z), one float4 of a block's
+// 32 NW x D context per thread, in the partials' register order. For a query
 // block split into chunks c with partials (C_c, m_c, l_c): M = max m_c,
 // w_c = 2^(m_c - M), C = sum w_c C_c / sum w_c l_c, LSE = M + log2(sum w_c
 // l_c), in chunk order.
-template <int D>
+template <int D, int NW>
 __global__ void __launch_bounds__(256) fa_fwd_combine_kernel(const FaArgs a) {
-  constexpr int NB = D / 32, PER = D / 8;
+  constexpr int NB = D / 32, PER = NW * D / 32, BQW = 32 * NW;
   const int blk = blockIdx.x / PER, z = blockIdx.y, beta = z / a.ar, head = z - (z / a.ar) * a.ar;
   int t0, t1;
-  fa::block_range(blk, a.s, false, t0, t1);
+  fa::block_range(blk, a.s, false, t0, t1, BQW);
   const int nch = cdiv(t1 - t0, a.ct);
   if (nch <= 1) return;
   const int j = (blockIdx.x - blk * PER) * 256 + threadIdx.x;  // float4 index in register order
   const int wave = j / (NB * 256), rem = j - wave * (NB * 256), nb = rem >> 8, jj = (rem >> 6) & 3,
             lane = rem & 63;
-  const int r = 32 * wave + (lane & 31), qrow = blk * fa::BQ + r;
+  const int r = 32 * wave + (lane & 31), qrow = blk * BQW + r;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
   if (qrow < a.s) {  // (rows past the sequence end: nothing to combine)
-    const float2* ml = reinterpret_cast<const float2*>(a.part + fa::part_slot(a.z, 0, 0, a.s, a.ct, D));
+    const float2* ml = reinterpret_cast<const float2*>(a.part + fa::part_slot(a.z, 0, 0, a.s, a.ct, D, BQW));
     float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[fa::part_slot(z, blk, c, a.s, a.ct, 1) + r].x);
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[fa::part_slot(z, blk, c, a.s, a.ct, 1, BQW) + r].x);
     float L = 0.0f;
     for (int c = 0; c < nch; ++c) {
-      const float2 x = ml[fa::part_slot(z, blk, c, a.s, a.ct, 1) + r];
+      const float2 x = ml[fa::part_slot(z, blk, c, a.s, a.ct, 1, BQW) + r];
       const float w = __builtin_amdgcn_exp2f(x.x - M);
       L += w * x.y;
-      const float4 p = reinterpret_cast<const float4*>(a.part + fa::part_slot(z, blk, c, a.s, a.ct, D))[j];
+      const float4 p =
+          reinterpret_cast<const float4*>(a.part + fa::part_slot(z, blk, c, a.s, a.ct, D, BQW))[j];
       v[0] += w * p.x; v[1] += w * p.y; v[2] += w * p.z; v[3] += w * p.w;
     }
     const float inv = 1.0f / L;
@@ -615,7 +612,7 @@ __global__ void __launch_bounds__(256) fa_fwd_combine_kernel(const FaArgs a) {
   st[lane & 31][c4] = make_float4(v[0], v[1], v[2], v[3]);
   __syncthreads();
   const int rr = threadIdx.x >> 3, cc = threadIdx.x & 7;
-  const int qrow2 = blk * fa::BQ + 32 * wave + rr;
+  const int qrow2 = blk * BQW + 32 * wave + rr;
   if (qrow2 < a.s) {
     const float4 x = st[rr][cc];
     const float w4[4] = {x.x, x.y, x.z, x.w};

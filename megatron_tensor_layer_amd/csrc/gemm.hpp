@@ -67,6 +67,8 @@ struct GemmArgs {
   int skm_base, skm_col0;  // first stream-K tile index; first tile-column of the stream-K region
   int skm_br, skm_bc;      // tiles of one XCD: a block of skm_br x skm_bc tiles
   int skm_q, skm_gr, skm_gc;  // runs of one K phase: skm_q groups of skm_gr x skm_gc tiles per block
+  int xcd_br, xcd_bc, xcd_g;  // > 0: XCD x takes one xcd_br x xcd_bc block of tiles (blocks laid out
+                             // row-major over the tile grid), walked in strips of xcd_g tile-rows
   int kseg, kseg_len;    // kseg = 3: K runs over (A,B), (A,B2), (A2,B), each kseg_len long
   int c2_cols;           // EPI_BIAS_SPLIT: columns that get a residual in C2
   const void* A; long lda, a_s1, a_s2;
@@ -390,6 +392,18 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn,
     const int gpr = p.skm_bc / p.skm_gc, bpr = p.tiles_m / p.skm_br;
     tm = (x % bpr) * p.skm_br + (d / gpr) * p.skm_gr + k % p.skm_gr;
     tn = p.skm_col0 + (x / bpr) * p.skm_bc + (d % gpr) * p.skm_gc + k / p.skm_gr;
+    return;
+  }
+  if (p.xcd_br > 0) {
+    // block L runs on XCD x = L mod 8 as its i-th block (i = L / 8): XCD x
+    // owns the x-th block of the grid, so the operand panels its tiles share
+    // stay in its own L2; inside the block, strips of xcd_g tile-rows,
+    // column by column
+    const int x = L & 7, i = L >> 3;
+    const int nbc = p.tiles_n / p.xcd_bc;
+    const int per = p.xcd_g * p.xcd_bc, grp = i / per, w = i - grp * per;
+    tm = (x / nbc) * p.xcd_br + grp * p.xcd_g + w % p.xcd_g;
+    tn = (x % nbc) * p.xcd_bc + w / p.xcd_g;
     return;
   }
   const int tiles = p.tiles_m * p.tiles_n;

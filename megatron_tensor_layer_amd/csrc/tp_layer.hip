@@ -209,21 +209,31 @@ bool flash(const Dims& D) {
   return D.d == 64 || D.d == 96 || D.d == 128 || D.d == 160;
 }
 
-// Flash attention chunk size: when the heads' query
-// blocks alone keep the CUs busy, blocks run whole; otherwise their tile
-// ranges are cut into chunks of 8 tiles (the causal ranges differ up to s /
-// 64 : 1 in length) and merged by a combine kernel.
-int fa_chunk_tiles(const Dims& D) {
-  const long nblk = cdivl(D.s, fa::BQ), ntot = cdivl(D.s, fa::BT);
-  if (D.z * nblk >= 4 * 256) return (int)(ntot + (ntot & 1));
+// Flash attention chunk size for blocks of bq rows when `slots` workgroups
+// run on the chip at once: when the heads' blocks alone keep them busy twice
+// over, blocks run whole; otherwise their tile ranges are cut into chunks of
+// 8 tiles (the causal ranges differ up to s / 64 : 1 in length) and merged by
+// a combine kernel. (8 is a multiple of bq / 64, so every query row sees the
+// first key of each chunk of its block.)
+int fa_chunk_tiles(const Dims& D, int bq, long slots) {
+  const long nblk = cdivl(D.s, bq), ntot = cdivl(D.s, fa::BT);
+  if (D.z * nblk >= 2 * slots) return (int)(ntot + (ntot & 1));
   return 8;
 }
+// Backward kernels: 128-row blocks; dK/dV one workgroup per CU, dQ two.
+int fa_chunk_tiles(const Dims& D) { return fa_chunk_tiles(D, fa::BQ, 2 * 256); }
+// Forward: 256-query blocks of 8 waves (one workgroup per CU) for d <= 128,
+// 128-query blocks of 4 waves for d = 160.
+int fa_fwd_bq(const Dims& D) { return D.d <= 128 ? fa::BQF : fa::BQ; }
+int fa_fwd_chunk_tiles(const Dims& D) { return fa_chunk_tiles(D, fa_fwd_bq(D), 256); }
 // fp32 partials of split blocks: forward C (+ m, l per row) or backward dK, dV
 // (the dQ partials reuse the region after the dK/dV combine).
 size_t fa_part_bytes(const Dims& D, int blk) {
-  const int ct = fa_chunk_tiles(D);
-  const size_t slots = (size_t)fa::part_slot((int)D.z, 0, 0, (int)D.s, ct, 1);  // z x blocks x chunks x 128
-  return blk == TP_ATTN ? 4 * slots * std::max<long>(D.d + 2, 2 * D.d) : 0;
+  if (blk != TP_ATTN) return 0;
+  // z x blocks x chunks x rows per block
+  const size_t fs = (size_t)fa::part_slot((int)D.z, 0, 0, (int)D.s, fa_fwd_chunk_tiles(D), 1, fa_fwd_bq(D));
+  const size_t bs = (size_t)fa::part_slot((int)D.z, 0, 0, (int)D.s, fa_chunk_tiles(D), 1);
+  return 4 * std::max<size_t>(fs * (D.d + 2), bs * 2 * D.d);
 }
 
 // ATTN keeps QKV, P and C (and, for bf16, C in fp32 for the softmax
@@ -632,6 +642,29 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
   return run<AK, BKM, EPI, ROLE, KIND_BIG>(D, p, 1, st);
 }
 
+// One block of tiles per XCD (GemmArgs xcd_*): when the tile grid splits into
+// 8 equal blocks, the split with the shortest block perimeter (the fewest
+// operand panels per XCD), walked in strips of g tile-rows (g dividing the
+// block's rows). In the grouped backward launches this keeps the panels
+// that an XCD's tiles share in its own L2: at the 175B shape the counter
+// traffic per launch falls from 1514 to 1211 MB (FC2), 1401 to 1136 MB
+// (FC1), 966 to 891 MB (QKV) and 604 to 453 MB (O) against the plain
+// grouped order (runs of 8 tile-rows), at the same speed.
+constexpr int kXcdStrip = 4;
+void xcd_blocks(GemmArgs& p, int g) {
+  int best = 1 << 30;
+  for (int nr = 1; nr <= 8; nr *= 2) {
+    const int nc = 8 / nr;
+    if (p.tiles_m % nr || p.tiles_n % nc) continue;
+    const int br = p.tiles_m / nr, bc = p.tiles_n / nc;
+    if (br % std::min(g, br) || br + bc >= best) continue;
+    best = br + bc;
+    p.xcd_br = br;
+    p.xcd_bc = bc;
+    p.xcd_g = std::min(g, br);
+  }
+}
+
 // A block's input-gradient GEMM (problem 0: dY W^T, K-contiguous operands,
 // epilogue E0) and weight-gradient GEMM (problem 1: X^T dY) in one launch
 // when both run on the direct bf16 kernel; otherwise two launches.
@@ -669,6 +702,8 @@ hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_
     q->splits = 1;
   }
   const int tiles0 = p0.tiles_m * p0.tiles_n, tiles1 = p1.tiles_m * p1.tiles_n;
+  xcd_blocks(p0, kXcdStrip);
+  xcd_blocks(p1, kXcdStrip);
   const PairPlan P = pair_plan(p0.M, p0.N, p0.K, p1.M, p1.N, p1.K, E0 == EPI_GELU_BWD);
   const int splits = P.splits;
   if (splits > 1) {
@@ -775,11 +810,9 @@ FaArgs fa_args(const Dims& D) {
       default: return hipErrorInvalidValue;                                                   \
     }                                                                                         \
   } while (0)
-// Head widths up to 128 run the forward and dQ kernels with single-buffered
-// tiles, two workgroups per CU (they fit 256 registers per lane); d = 160 and
-// the dK/dV kernel keep one double-buffered workgroup per CU.
-#define TPL_FA_FWD(DD) (DD <= 128 ? fa_fwd2_kernel<DD> : fa_fwd_kernel<DD>)
-#define TPL_FA_FWD_COMBINE(DD) fa_fwd_combine_kernel<DD>
+// Head widths up to 128 run the dQ kernel with single-buffered tiles, two
+// workgroups per CU (it fits 256 registers per lane); d = 160 and the dK/dV
+// kernel keep one double-buffered workgroup per CU.
 #define TPL_FA_DKV(DD) fa_bwd_dkv_kernel<DD>
 #define TPL_FA_DQ(DD) (DD <= 128 ? fa_bwd_dq2_kernel<DD> : fa_bwd_dq_kernel<DD>)
 #define TPL_FA_KV_COMBINE(DD) (fa_bwd_combine_kernel<DD, true>)
@@ -789,9 +822,31 @@ bool fa_split(const Dims& D, const FaArgs& a) { return a.ct < cdivl(D.s, fa::BT)
 dim3 fa_combine_grid(const Dims& D) { return dim3((unsigned)(cdivl(D.s, fa::BQ) * (D.d / 8)), (unsigned)D.z); }
 
 hipError_t fa_fwd(const Dims& D, FaArgs a, hipStream_t st) {
-  a.items = fa::items_per_head(a.s, a.ct, false);
-  TPL_FA_SWITCH(TPL_FA_FWD, dim3((unsigned)(a.z * a.items)));
-  if (fa_split(D, a)) TPL_FA_SWITCH(TPL_FA_FWD_COMBINE, fa_combine_grid(D));
+  const int bq = fa_fwd_bq(D);
+  a.ct = fa_fwd_chunk_tiles(D);
+  a.items = fa::items_per_head(a.s, a.ct, false, bq);
+  const dim3 grid((unsigned)(a.z * a.items));
+  const dim3 cgrid((unsigned)(cdivl(D.s, bq) * (bq / 32) * (D.d / 32)), (unsigned)D.z);
+  const bool split = fa_split(D, a);
+  switch (D.d) {
+    case 64:
+      hipLaunchKernelGGL(fa_fwd8_kernel<64>, grid, dim3(512), 0, st, a);
+      if (split) hipLaunchKernelGGL((fa_fwd_combine_kernel<64, 8>), cgrid, dim3(256), 0, st, a);
+      break;
+    case 96:
+      hipLaunchKernelGGL(fa_fwd8_kernel<96>, grid, dim3(512), 0, st, a);
+      if (split) hipLaunchKernelGGL((fa_fwd_combine_kernel<96, 8>), cgrid, dim3(256), 0, st, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(fa_fwd8_kernel<128>, grid, dim3(512), 0, st, a);
+      if (split) hipLaunchKernelGGL((fa_fwd_combine_kernel<128, 8>), cgrid, dim3(256), 0, st, a);
+      break;
+    case 160:
+      hipLaunchKernelGGL(fa_fwd_kernel<160>, grid, dim3(256), 0, st, a);
+      if (split) hipLaunchKernelGGL((fa_fwd_combine_kernel<160, 4>), cgrid, dim3(256), 0, st, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 hipError_t fa_dkv(const Dims& D, FaArgs a, hipStream_t st) {
