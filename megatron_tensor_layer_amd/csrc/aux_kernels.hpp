@@ -180,7 +180,16 @@ __global__ void __launch_bounds__(256) splitk_rowdot_kernel(const float* __restr
     for (int c = threadIdx.x; c < nc; c += 256) {
       const long off = (long)row * ld + (long)h0 * d + 4 * c;
       float u[4] = {0.f, 0.f, 0.f, 0.f}, v[4];
-      for (int k = 0; k < splits; ++k) {
+      // pieces in order, two loads in flight per step
+      int k = 0;
+      for (; k + 2 <= splits; k += 2) {
+        float x[4], y[4];
+        Elt<float>::load4(part + (long)k * T * ld + off, x);
+        Elt<float>::load4(part + (long)(k + 1) * T * ld + off, y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = (u[e] + x[e]) + y[e];
+      }
+      if (k < splits) {
         float x[4];
         Elt<float>::load4(part + (long)k * T * ld + off, x);
 #pragma unroll

@@ -591,14 +591,24 @@ __global__ void __launch_bounds__(256) fa_fwd_combine_kernel(const FaArgs a) {
     float M = -INFINITY;
     for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[fa::part_slot(z, blk, c, a.s, a.ct, 1, BQW) + r].x);
     float L = 0.0f;
-    for (int c = 0; c < nch; ++c) {
-      const float2 x = ml[fa::part_slot(z, blk, c, a.s, a.ct, 1, BQW) + r];
+    // chunks in order; all of a chunk pair's loads go out before its sums
+    auto part4 = [&](int c) {
+      return reinterpret_cast<const float4*>(a.part + fa::part_slot(z, blk, c, a.s, a.ct, D, BQW))[j];
+    };
+    auto add = [&](const float2 x, const float4 p) {
       const float w = __builtin_amdgcn_exp2f(x.x - M);
       L += w * x.y;
-      const float4 p =
-          reinterpret_cast<const float4*>(a.part + fa::part_slot(z, blk, c, a.s, a.ct, D, BQW))[j];
       v[0] += w * p.x; v[1] += w * p.y; v[2] += w * p.z; v[3] += w * p.w;
+    };
+    int c = 0;
+    for (; c + 2 <= nch; c += 2) {
+      const float2 x0 = ml[fa::part_slot(z, blk, c, a.s, a.ct, 1, BQW) + r];
+      const float2 x1 = ml[fa::part_slot(z, blk, c + 1, a.s, a.ct, 1, BQW) + r];
+      const float4 p0 = part4(c), p1 = part4(c + 1);
+      add(x0, p0);
+      add(x1, p1);
     }
+    if (c < nch) add(ml[fa::part_slot(z, blk, c, a.s, a.ct, 1, BQW) + r], part4(c));
     const float inv = 1.0f / L;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= inv;
@@ -952,9 +962,18 @@ __global__ void __launch_bounds__(256) fa_bwd_combine_kernel(const FaArgs a) {
   for (int mat = 0; mat < MATS; ++mat) {
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (row < a.s) {
-      for (int c = 0; c < nch; ++c) {
-        const float4 x = reinterpret_cast<const float4*>(a.part + MATS * fa::part_slot(z, blk, c, a.s, a.ct, D) +
-                                                         mat * fa::BQ * D)[j];
+      // chunks in order, two loads in flight per step
+      auto part4 = [&](int c) {
+        return reinterpret_cast<const float4*>(a.part + MATS * fa::part_slot(z, blk, c, a.s, a.ct, D) +
+                                               mat * fa::BQ * D)[j];
+      };
+      int c = 0;
+      for (; c + 2 <= nch; c += 2) {
+        const float4 x = part4(c), y = part4(c + 1);
+        v[0] = (v[0] + x.x) + y.x; v[1] = (v[1] + x.y) + y.y; v[2] = (v[2] + x.z) + y.z; v[3] = (v[3] + x.w) + y.w;
+      }
+      if (c < nch) {
+        const float4 x = part4(c);
         v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
       }
     }

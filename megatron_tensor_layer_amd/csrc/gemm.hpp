@@ -592,7 +592,16 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
   if (idx >= (long)p.M * n4) return;
   const int row = (int)(idx / n4), col = (int)(idx - (idx / n4) * n4) * 4;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.splits; ++s) {
+  // pieces in order, two loads in flight per step
+  int s = 0;
+  for (; s + 2 <= p.splits; s += 2) {
+    float x[4], y[4];
+    Elt<float>::load4(p.part + ((long)s * p.M + row) * (long)p.N + col, x);
+    Elt<float>::load4(p.part + ((long)(s + 1) * p.M + row) * (long)p.N + col, y);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (v[e] + x[e]) + y[e];
+  }
+  if (s < p.splits) {
     float x[4];
     Elt<float>::load4(p.part + ((long)s * p.M + row) * (long)p.N + col, x);
 #pragma unroll

@@ -462,7 +462,17 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(const GemmArgs p, const S
   const int uf = (int)(((long)j * s.iters) / s.c), ul = (int)(((long)(j + 1) * s.iters - 1) / s.c);
   const float* src = s.part + (long)j * s.f * (BM * BN) + (long)rt * BN + ct;
   float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k <= ul - uf; ++k) {
+  // fragments in slot order, two loads in flight per step
+  const int nf = ul - uf + 1;
+  int k = 0;
+  for (; k + 2 <= nf; k += 2) {
+    float x[8], y[8];
+    loadv<float, 8>(src + (long)k * (BM * BN), x);
+    loadv<float, 8>(src + (long)(k + 1) * (BM * BN), y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (v[e] + x[e]) + y[e];
+  }
+  if (k < nf) {
     float x[8];
     loadv<float, 8>(src + (long)k * (BM * BN), x);
 #pragma unroll

@@ -645,11 +645,12 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
 // One block of tiles per XCD (GemmArgs xcd_*): when the tile grid splits into
 // 8 equal blocks, the split with the shortest block perimeter (the fewest
 // operand panels per XCD), walked in strips of g tile-rows (g dividing the
-// block's rows). In the grouped backward launches this keeps the panels
-// that an XCD's tiles share in its own L2: at the 175B shape the counter
-// traffic per launch falls from 1514 to 1211 MB (FC2), 1401 to 1136 MB
-// (FC1), 966 to 891 MB (QKV) and 604 to 453 MB (O) against the plain
-// grouped order (runs of 8 tile-rows), at the same speed.
+// block's rows). Used for the weight-gradient problem of the grouped
+// backward launches, whose K = T tiles are many and short: an XCD's tiles
+// then share their operand panels in its own L2, which cuts the launch's
+// counter traffic at the same or slightly better speed. (For the
+// input-gradient problem, long-K tiles that start together, the plain runs
+// of tile-rows measured faster.)
 constexpr int kXcdStrip = 4;
 void xcd_blocks(GemmArgs& p, int g) {
   int best = 1 << 30;
@@ -702,7 +703,6 @@ hipError_t pair(const Dims& D, GemmArgs p0, GemmArgs p1, float* part, hipStream_
     q->splits = 1;
   }
   const int tiles0 = p0.tiles_m * p0.tiles_n, tiles1 = p1.tiles_m * p1.tiles_n;
-  xcd_blocks(p0, kXcdStrip);
   xcd_blocks(p1, kXcdStrip);
   const PairPlan P = pair_plan(p0.M, p0.N, p0.K, p1.M, p1.N, p1.K, E0 == EPI_GELU_BWD);
   const int splits = P.splits;
@@ -814,7 +814,12 @@ FaArgs fa_args(const Dims& D) {
 // workgroups per CU (it fits 256 registers per lane); d = 160 and the dK/dV
 // kernel keep one double-buffered workgroup per CU.
 #define TPL_FA_DKV(DD) fa_bwd_dkv_kernel<DD>
-#define TPL_FA_DQ(DD) (DD <= 128 ? fa_bwd_dq2_kernel<DD> : fa_bwd_dq_kernel<DD>)
+template <int DD>
+constexpr auto fa_dq_kernel() {
+  if constexpr (DD <= 128) return fa_bwd_dq2_kernel<DD>;
+  else return fa_bwd_dq_kernel<DD>;
+}
+#define TPL_FA_DQ(DD) (fa_dq_kernel<DD>())
 #define TPL_FA_KV_COMBINE(DD) (fa_bwd_combine_kernel<DD, true>)
 #define TPL_FA_Q_COMBINE(DD) (fa_bwd_combine_kernel<DD, false>)
 
