@@ -340,6 +340,29 @@ __device__ __forceinline__ void row_products(const uint4* L, const LaneOff& lo, 
   }
 }
 
+// row_products with f(ks) called after the MFMAs of each step (inside its
+// scheduling region): independent VALU work placed there runs while the
+// matrix pipe works through those MFMAs.
+template <int KS, class F>
+__device__ __forceinline__ void row_products_with(const uint4* L, const LaneOff& lo, const uint4 (&x)[KS],
+                                                  f32x16_t (&acc)[2], F&& f) {
+  uint4 fr[2][2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) fr[0][bb] = frag16(L, lo, 0, bb);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) fr[cur ^ 1][bb] = frag16(L, lo, ks + 1, bb);
+    }
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) mma16(fr[cur][bb], x[ks], acc[bb], bf16_t{});
+    f(ks);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // out[nb] += P . Y over the tile's 64 rows, P given as fp32 accumulators
 // p[2] (rows x 64, converted to bf16 here) and Y (64 x NB*32) read
 // transposed from LDS, one 16-row step ahead.
@@ -359,6 +382,28 @@ __device__ __forceinline__ void tr_products(const uint4* L, const LaneOff& lo, c
     const uint4 pf = pack_frag(p[kk >> 1], kk & 1);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) mma16(y[cur][nb], pf, out[nb], bf16_t{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// tr_products with f(kk) called after the MFMAs of each 16-row step.
+template <int NB, class F>
+__device__ __forceinline__ void tr_products_with(const uint4* L, const LaneOff& lo, const f32x16_t (&p)[2],
+                                                 f32x16_t (&out)[NB], F&& f) {
+  uint4 y[2][NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) y[0][nb] = frag_tr(L, lo, 0, nb);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < 4) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) y[cur ^ 1][nb] = frag_tr(L, lo, kk + 1, nb);
+    }
+    const uint4 pf = pack_frag(p[kk >> 1], kk & 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) mma16(y[cur][nb], pf, out[nb], bf16_t{});
+    f(kk);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -721,40 +766,63 @@ fa_bwd_dkv_kernel(const FaArgs a) {
       fa::zero(st[0]);
       fa::zero(st[1]);
       fa::split_scores<KS>(Lq, Lq + TL::U4, lo, kh, kl, st);
-      // P^T (keys x queries), visible iff key <= query < s
-      // (tiles clear of the diagonal and the sequence end take a branch-free
-      // loop; a per-element mask would become one branch per element)
-      if (fa::BT * t < kmin + 32 || fa::BT * t + fa::BT > a.s) {
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int c = fa::acc_col(bb, e, g), q = fa::BT * t + c;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][e], a.sl2, -Lf[c]));
-            st[bb][e] = (q < krow || q >= a.s) ? 0.0f : p;
-          }
-      } else {
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int c = fa::acc_col(bb, e, g);
-            st[bb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][e], a.sl2, -Lf[c]));
-          }
-      }
-      fa::tr_products<NB>(Ld, lo, st, dv);  // dV += P^T dC
-      // dP^T = V dC^T;  dS^T = P^T (dP^T - D) / sqrt(d)
+      // P^T (keys x queries), visible iff key <= query < s.  Tiles clear of
+      // the diagonal and the sequence end take the unmasked form (a runtime
+      // per-element mask would become one branch per element).
+      auto expo = [&](auto masked, int i) {
+        const int bb = i >> 4, e = i & 15;
+        const int c = fa::acc_col(bb, e, g);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][e], a.sl2, -Lf[c]));
+        if constexpr (decltype(masked)::value) {
+          const int q = fa::BT * t + c;
+          st[bb][e] = (q < krow || q >= a.s) ? 0.0f : p;
+        } else {
+          st[bb][e] = p;
+        }
+      };
+      const bool edge = fa::BT * t < kmin + 32 || fa::BT * t + fa::BT > a.s;
+      // dS^T = P^T (dP^T - D) / sqrt(d), in place of dP^T
       f32x16_t dp[2];
+      auto dsi = [&](int i) {
+        const int bb = i >> 4, e = i & 15;
+        const int c = fa::acc_col(bb, e, g);
+        dp[bb][e] = st[bb][e] * a.sc * (dp[bb][e] - Lf[64 + c]);
+      };
       fa::zero(dp[0]);
       fa::zero(dp[1]);
-      fa::row_products<KS>(Ld, lo, vf, dp);
+      if constexpr (D <= 128) {
+        // dP^T = V dC^T does not depend on the scores, so its MFMAs go first
+        // with the exponentials spread over its steps, and dS^T is formed
+        // under the MFMAs of dV += P^T dC: the VALU work runs while the
+        // matrix pipe is busy instead of between the products.
+        constexpr int EPS = (32 + KS - 1) / KS;  // exponentials per dP^T step
+        auto run = [&](auto masked) {
+          fa::row_products_with<KS>(Ld, lo, vf, dp, [&](int ks) {
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+            for (int j = 0; j < EPS; ++j)
+              if (ks * EPS + j < 32) expo(masked, ks * EPS + j);
+          });
+        };
+        if (edge) run(std::true_type{});
+        else run(std::false_type{});
+        fa::tr_products_with<NB>(Ld, lo, st, dv, [&](int kk) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int c = fa::acc_col(bb, e, g);
-          dp[bb][e] = st[bb][e] * a.sc * (dp[bb][e] - Lf[64 + c]);
-        }
+          for (int j = 0; j < 8; ++j) dsi(kk * 8 + j);
+        });
+      } else {
+        // d = 160: the registers leave no room to hold dP^T through dV's
+        // products, so the steps run in dependency order.
+        auto run = [&](auto masked) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) expo(masked, i);
+        };
+        if (edge) run(std::true_type{});
+        else run(std::false_type{});
+        fa::tr_products<NB>(Ld, lo, st, dv);  // dV += P^T dC
+        fa::row_products<KS>(Ld, lo, vf, dp);  // dP^T = V dC^T
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dsi(i);
+      }
       fa::tr_products<NB>(Lq, lo, dp, dk);  // dK += dS^T Qh
     }
     wait_loads();
