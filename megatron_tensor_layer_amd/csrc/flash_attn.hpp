@@ -242,7 +242,28 @@ __device__ __forceinline__ void zero(f32x16_t& a) {
   for (int e = 0; e < 16; ++e) a[e] = 0.0f;
 }
 
-__device__ __forceinline__ float xlane32(float v) { return __shfl_xor(v, 32, 64); }
+// v combined with the value of lane l ^ 32 (the other half of the row's
+// columns), in the same order on both lanes (the operations are
+// commutative): v_permlane32_swap exchanges the two 32-lane halves between
+// two registers in the VALU, without an LDS round trip.
+// (Written as assembly: the compiler's builtin for this instruction loses its
+// second result. The s_nop covers the wait states the instruction needs after
+// a VALU write of its operands.)
+__device__ __forceinline__ void halves(float v, float& lo, float& hi) {
+  lo = v;
+  hi = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+__device__ __forceinline__ float max32(float v) {
+  float lo, hi;
+  halves(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum32(float v) {
+  float lo, hi;
+  halves(v, lo, hi);
+  return lo + hi;
+}
 
 // Column (within a 64-wide tile) of accumulator register e of block bb.
 __device__ __forceinline__ int acc_col(int bb, int e, int g) { return 32 * bb + 8 * (e >> 2) + 4 * g + (e & 3); }
@@ -546,7 +567,7 @@ __device__ __forceinline__ void fa_fwd_body(const FaArgs& a, uint4* lds) {
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[bb][e]);
-      mx = fmaxf(mx, fa::xlane32(mx)) * a.sl2;  // row maximum of the tile, log2 units
+      mx = fa::max32(mx) * a.sl2;  // row maximum of the tile, log2 units
       const bool grow = mx > m + fa::TAU;      // (true on the chunk's first tile: m = -inf)
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float mn = grow ? mx : m;
@@ -567,7 +588,7 @@ __device__ __forceinline__ void fa_fwd_body(const FaArgs& a, uint4* lds) {
           sacc[bb][e] = p;
           rs += p;
         }
-      l += rs + fa::xlane32(rs);
+      l += fa::sum32(rs);
       fa::tr_products<NB>(Lk + 2 * TL::U4, lo, sacc, o);
     }
   };
