@@ -350,6 +350,75 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
     }
   }
 
+  // bf16 output of the plain epilogue (no residual term): scale and bias are
+  // applied in registers and the tile is staged through LDS already rounded
+  // to bf16, two 32-row blocks of every wave per pass (half the LDS traffic
+  // and half the passes of the fp32 staging below; the same operations and
+  // the same single rounding per element). 16-byte chunk q of staged row r
+  // sits at chunk q ^ (r mod C16), so the 32 rows a write instruction
+  // touches, and the chunks of one row that a read instruction takes, fall
+  // on distinct banks.
+  if constexpr (EPI == EPI_LINEAR && std::is_same<TO, bf16_t>::value && TM % 2 == 0) {
+    if (!p.resid) {
+      constexpr int C16 = BN / 8;            // 16-byte chunks per staged row
+      constexpr int PR2 = 2 * Cfg::WM * 32;  // rows staged per pass
+      constexpr int PER2 = PR2 * C16 / NT;   // chunks per thread and pass
+      static_assert((C16 & (C16 - 1)) == 0 && (PR2 * C16) % NT == 0, "bf16 staging layout");
+      static_assert(PR2 * BN * 2 <= 2 * (BM + BN) * 128, "staging must fit the operand buffers");
+      __syncthreads();  // every wave is past its last fragment read and LDS load
+      unsigned char* const st8 = reinterpret_cast<unsigned char*>(sa0);
+      const int r32 = lane & 31, g = lane >> 5;
+      bf16_t* const C = static_cast<bf16_t*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2;
+#pragma unroll
+      for (int pp = 0; pp < TM / 2; ++pp) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ps = 2 * pp + h, rl = h * (Cfg::WM * 32) + wm * 32 + r32;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int cb = wn * WTN + j * 32 + jj * 8;  // the lane's 4 columns: cb + 4 g ..
+              float v[4] = {acc[ps][j][4 * jj], acc[ps][j][4 * jj + 1], acc[ps][j][4 * jj + 2],
+                            acc[ps][j][4 * jj + 3]};
+              // (copied out here, so that the accumulators themselves are
+              // used only by MFMAs and stay in the accumulation registers)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
+              if (p.alpha != 1.0f) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= p.alpha;
+              }
+              if (p.bias && n0 + cb + 4 * g < p.N) {
+                float bb[4];
+                loadv<bf16_t, 4>(static_cast<const bf16_t*>(p.bias) + n0 + cb + 4 * g, bb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bb[e];
+              }
+              const f32x4_t x = {v[0], v[1], v[2], v[3]};
+              *reinterpret_cast<bf16x4_t*>(st8 + rl * (BN * 2) + (((cb >> 3) ^ (rl & (C16 - 1))) << 4) + 8 * g) =
+                  __builtin_convertvector(x, bf16x4_t);
+              // (one group at a time: hoisted accumulator reads would take
+              // more registers than the wave has left)
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER2; ++k) {
+          const int c = tid + k * NT;
+          const int rs = c / C16, q = c - (c / C16) * C16;
+          const uint4 x = *reinterpret_cast<const uint4*>(st8 + rs * (BN * 2) + ((q ^ (rs & (C16 - 1))) << 4));
+          const int h = rs / (Cfg::WM * 32), r = rs - h * (Cfg::WM * 32);
+          const int row = m0 + (r >> 5) * WTM + (2 * pp + h) * 32 + (r & 31), col = n0 + 8 * q;
+          if (row < p.M && col < p.N) *reinterpret_cast<uint4*>(C + (long)row * p.ldc + col) = x;
+        }
+        if (pp + 1 < TM / 2) __syncthreads();
+      }
+      return;
+    }
+  }
+
   // Epilogue through LDS. Stored straight from the MFMA layout, a lane holds
   // 4 columns of one row and a store instruction touches 32 rows, which
   // serialises on the memory channel whenever the row pitch is a large power
