@@ -369,8 +369,11 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
       unsigned char* const st8 = reinterpret_cast<unsigned char*>(sa0);
       const int r32 = lane & 31, g = lane >> 5;
       bf16_t* const C = static_cast<bf16_t*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2;
-#pragma unroll
-      for (int pp = 0; pp < TM / 2; ++pp) {
+      // (the scale and bias are uniform: with neither, the pass is a
+      // conversion and one 8-byte LDS write per 4 values, without the
+      // per-element selects and guarded bias loads of the general form)
+      const bool plain = p.alpha == 1.0f && !p.bias;
+      auto write_pass = [&](int pp, auto general) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int ps = 2 * pp + h, rl = h * (Cfg::WM * 32) + wm * 32 + r32;
@@ -385,24 +388,28 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
               // used only by MFMAs and stay in the accumulation registers)
 #pragma unroll
               for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
-              if (p.alpha != 1.0f) {
+              if constexpr (decltype(general)::value) {
+                if (p.alpha != 1.0f) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] *= p.alpha;
-              }
-              if (p.bias && n0 + cb + 4 * g < p.N) {
-                float bb[4];
-                loadv<bf16_t, 4>(static_cast<const bf16_t*>(p.bias) + n0 + cb + 4 * g, bb);
+                  for (int e = 0; e < 4; ++e) v[e] *= p.alpha;
+                }
+                if (p.bias && n0 + cb + 4 * g < p.N) {
+                  float bb[4];
+                  loadv<bf16_t, 4>(static_cast<const bf16_t*>(p.bias) + n0 + cb + 4 * g, bb);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] += bb[e];
+                  for (int e = 0; e < 4; ++e) v[e] += bb[e];
+                }
               }
               const f32x4_t x = {v[0], v[1], v[2], v[3]};
               *reinterpret_cast<bf16x4_t*>(st8 + rl * (BN * 2) + (((cb >> 3) ^ (rl & (C16 - 1))) << 4) + 8 * g) =
                   __builtin_convertvector(x, bf16x4_t);
-              // (one group at a time: hoisted accumulator reads would take
-              // more registers than the wave has left)
-              __builtin_amdgcn_sched_barrier(0);
             }
         }
+      };
+#pragma unroll
+      for (int pp = 0; pp < TM / 2; ++pp) {
+        if (plain) write_pass(pp, std::false_type{});
+        else write_pass(pp, std::true_type{});
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < PER2; ++k) {
