@@ -373,6 +373,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
       // conversion and one 8-byte LDS write per 4 values, without the
       // per-element selects and guarded bias loads of the general form)
       const bool plain = p.alpha == 1.0f && !p.bias;
+      const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
       auto write_pass = [&](int pp, auto general) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -411,14 +412,37 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
         if (plain) write_pass(pp, std::false_type{});
         else write_pass(pp, std::true_type{});
         __syncthreads();
-#pragma unroll
-        for (int k = 0; k < PER2; ++k) {
+        auto chunk = [&](int k, int& row, int& col) {
           const int c = tid + k * NT;
           const int rs = c / C16, q = c - (c / C16) * C16;
-          const uint4 x = *reinterpret_cast<const uint4*>(st8 + rs * (BN * 2) + ((q ^ (rs & (C16 - 1))) << 4));
           const int h = rs / (Cfg::WM * 32), r = rs - h * (Cfg::WM * 32);
-          const int row = m0 + (r >> 5) * WTM + (2 * pp + h) * 32 + (r & 31), col = n0 + 8 * q;
-          if (row < p.M && col < p.N) *reinterpret_cast<uint4*>(C + (long)row * p.ldc + col) = x;
+          row = m0 + (r >> 5) * WTM + (2 * pp + h) * 32 + (r & 31);
+          col = n0 + 8 * q;
+          return *reinterpret_cast<const uint4*>(st8 + rs * (BN * 2) + ((q ^ (rs & (C16 - 1))) << 4));
+        };
+        if (full) {
+          // whole tile: no guards; one LDS read ahead of each store (a
+          // burst of all the pass's stores at once runs slower)
+          int row, col;
+          uint4 x = chunk(0, row, col);
+#pragma unroll
+          for (int k = 0; k < PER2; ++k) {
+            int row1 = 0, col1 = 0;
+            uint4 x1;
+            if (k + 1 < PER2) x1 = chunk(k + 1, row1, col1);
+            *reinterpret_cast<uint4*>(C + (long)row * p.ldc + col) = x;
+            __builtin_amdgcn_sched_barrier(0);
+            x = x1;
+            row = row1;
+            col = col1;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < PER2; ++k) {
+            int row, col;
+            const uint4 x = chunk(k, row, col);
+            if (row < p.M && col < p.N) *reinterpret_cast<uint4*>(C + (long)row * p.ldc + col) = x;
+          }
         }
         if (pp + 1 < TM / 2) __syncthreads();
       }
