@@ -470,6 +470,19 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 #pragma unroll
   for (int ps = 0; ps < TM; ++ps) {
     const int rl = wm * 32 + r32;
+    // GELU backward: the pass's U values are loaded ahead of the staging, so
+    // that their latency passes under it (rows and columns clamped into the
+    // matrix; the stores below stay guarded)
+    uint4 ux[EPI == EPI_GELU_BWD ? PER : 1];
+    if constexpr (EPI == EPI_GELU_BWD) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int c = tid + k * NT;
+        const int rs = c / C8, q = c - (c / C8) * C8;
+        const int row = min(m0 + (rs >> 5) * WTM + ps * 32 + (rs & 31), p.M - 1), col = min(n0 + 8 * q, p.N - 8);
+        ux[k] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(p.aux) + (long)row * p.ldx + col);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -489,6 +502,15 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
       const int rt = (rs >> 5) * WTM + ps * 32 + (rs & 31);  // row within the tile
       if constexpr (EPI == EPI_SK_PART) {
         storev<float, 8>(skdst + rt * BN + 8 * q, v);  // the unit's fragment, tile-row-major
+      } else if constexpr (EPI == EPI_GELU_BWD) {
+        const int row = m0 + rt, col = n0 + 8 * q;
+        if (row < p.M && col < p.N) {
+          const uint32_t w[4] = {ux[k].x, ux[k].y, ux[k].z, ux[k].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            v[e] *= gelu_grad_f(__uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16)));
+          storev<TO, 8>(static_cast<TO*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
+        }
       } else {
         const int row = m0 + rt, col = n0 + 8 * q;
         if (row < p.M && col < p.N) epi_apply<EPI, bf16_t, TO, 8>(p, z1, z2, row, col, v, split);
