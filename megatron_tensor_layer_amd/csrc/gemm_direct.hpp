@@ -467,6 +467,12 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   __syncthreads();  // every wave is past its last fragment read and LDS load
   float4* stage = reinterpret_cast<float4*>(sa0);
   const int r32 = lane & 31, g = lane >> 5;
+  // Bias + split output: a thread's chunks all sit in the same 8 columns
+  // (NT is a multiple of the chunks per row), so their bias is loaded once,
+  // here, rather than once per chunk behind each chunk's LDS read.
+  constexpr bool PRE_BIAS = EPI == EPI_BIAS_SPLIT && NT % C8 == 0;
+  float bpre[PRE_BIAS ? 8 : 1];
+  if constexpr (PRE_BIAS) loadv<bf16_t, 8>(static_cast<const bf16_t*>(p.bias) + min(n0 + 8 * (tid % C8), p.N - 8), bpre);
 #pragma unroll
   for (int ps = 0; ps < TM; ++ps) {
     const int rl = wm * 32 + r32;
@@ -509,6 +515,19 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             v[e] *= gelu_grad_f(__uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16)));
+          storev<TO, 8>(static_cast<TO*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
+        }
+      } else if constexpr (PRE_BIAS) {
+        const int row = m0 + rt, col = n0 + 8 * q;
+        if (row < p.M && col < p.N) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += bpre[e];
+          if (col < p.c2_cols) {
+            float lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
+            storev<bf16_t, 8>(static_cast<bf16_t*>(p.C2) + (long)row * p.ldc2 + col, lo);
+          }
           storev<TO, 8>(static_cast<TO*>(p.C) + z1 * p.c_s1 + z2 * p.c_s2 + (long)row * p.ldc + col, v);
         }
       } else {
