@@ -467,10 +467,10 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   __syncthreads();  // every wave is past its last fragment read and LDS load
   float4* stage = reinterpret_cast<float4*>(sa0);
   const int r32 = lane & 31, g = lane >> 5;
-  // Bias + split output: a thread's chunks all sit in the same 8 columns
-  // (NT is a multiple of the chunks per row), so their bias is loaded once,
-  // here, rather than once per chunk behind each chunk's LDS read.
-  constexpr bool PRE_BIAS = EPI == EPI_BIAS_SPLIT && NT % C8 == 0;
+  // Bias epilogues: a thread's chunks all sit in the same 8 columns (NT is a
+  // multiple of the chunks per row), so their bias is loaded once, here,
+  // rather than once per chunk behind each chunk's LDS read.
+  constexpr bool PRE_BIAS = (EPI == EPI_BIAS_SPLIT || EPI == EPI_BIAS_GELU) && NT % C8 == 0;
   float bpre[PRE_BIAS ? 8 : 1];
   if constexpr (PRE_BIAS) loadv<bf16_t, 8>(static_cast<const bf16_t*>(p.bias) + min(n0 + 8 * (tid % C8), p.N - 8), bpre);
 #pragma unroll
@@ -522,7 +522,12 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
         if (row < p.M && col < p.N) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += bpre[e];
-          if (col < p.c2_cols) {
+          if constexpr (EPI == EPI_BIAS_GELU) {
+            float gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[e] = gelu_f(v[e]);
+            storev<bf16_t, 8>(static_cast<bf16_t*>(p.C2) + (long)row * p.ldc2 + col, gv);
+          } else if (col < p.c2_cols) {
             float lo[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
