@@ -31,9 +31,10 @@ def _need_gpu(gpu):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("ak,bk", [(1, 0), (1, 1), (0, 0), (0, 1)])
-@pytest.mark.parametrize("M,N,K", [(272, 400, 336), (16, 32, 48), (528, 256, 1040)])
-def test_gemm_layouts(dtype, ak, bk, M, N, K):
-    print(f"gemm {dtype} ak={ak} bk={bk} {M}x{N}x{K}", flush=True)
+@pytest.mark.parametrize("M,N,K", [(272, 400, 336), (16, 32, 48), (528, 256, 1040), (528, 520, 256)])
+@pytest.mark.parametrize("alpha,with_bias", [(0.5, True), (1.0, False)])  # scaled + bias, and the plain epilogue
+def test_gemm_layouts(dtype, ak, bk, M, N, K, alpha, with_bias):
+    print(f"gemm {dtype} ak={ak} bk={bk} {M}x{N}x{K} alpha={alpha} bias={with_bias}", flush=True)
     cfg = I.make_config("gemm", 64, 4, 32, 2, 1, dtype)
     rng = np.random.default_rng(M * 7 + N * 3 + K + ak * 2 + bk)
     A = rng.standard_normal((M, K)).astype(np.float32)
@@ -41,11 +42,12 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K):
     bias = rng.standard_normal(N).astype(np.float32)
     if dtype == "bf16":
         A, B, bias = I.round_to_bf16(A), I.round_to_bf16(B), I.round_to_bf16(bias)
-    ref = 0.5 * (A.astype(np.float64) @ B.astype(np.float64)) + bias
+    ref = alpha * (A.astype(np.float64) @ B.astype(np.float64)) + (bias if with_bias else 0.0)
     Ad = to_dev(A if ak else A.T, cfg)
     Bd = to_dev(B.T if bk else B, cfg)
     C = torch.full((M, N), float("nan"), device="cuda", dtype=tp.torch_dtype(dtype_code(cfg)))
-    tp.tp_gemm(dtype_code(cfg), M, N, K, 0.5, Ad, K if ak else M, ak, Bd, K if bk else N, bk, to_dev(bias, cfg), C, N)
+    tp.tp_gemm(dtype_code(cfg), M, N, K, alpha, Ad, K if ak else M, ak, Bd, K if bk else N, bk,
+               to_dev(bias, cfg) if with_bias else None, C, N)
     torch.cuda.synchronize()
     # bf16 output rounding (2^-9) plus fp32 accumulation; fp32: accumulation only
     tol = 8e-3 if dtype == "bf16" else 1e-5
