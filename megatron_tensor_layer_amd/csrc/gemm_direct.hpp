@@ -92,7 +92,9 @@ __device__ __forceinline__ int kswz(int row) {
 // LDS cycle.
 __device__ __forceinline__ int tsw(int k) { return (0x7520 >> (4 * (k & 3))) & 0xF; }
 
-template <bool KMAJ, int R, int NT>
+// VALID < R (M/N-major only): the tile is laid out R wide but only its first
+// VALID columns are loaded; lanes whose chunk lies beyond them issue no load.
+template <bool KMAJ, int R, int NT, int VALID = R>
 struct DirectOperand {
   static constexpr int BK = 64;
   static constexpr int TILE_BYTES = R * BK * 2;
@@ -102,9 +104,13 @@ struct DirectOperand {
   static constexpr int PER_WAVE = INSTS / WAVES;
   static constexpr int ROW_UNITS = R / 8;  // 16-byte units per k-row (M/N-major)
   static_assert(KMAJ || 64 % ROW_UNITS == 0, "an M/N-major load instruction covers whole k-rows of the tile");
+  static_assert(VALID == R || (!KMAJ && VALID % 8 == 0 && VALID < R), "partial loads: M/N-major tiles only");
+  static_assert(PER_WAVE <= 32, "one mask bit per load");
   uint32_t off[PER_WAVE];                  // element offsets at the tile's k origin
+  uint32_t live;                           // VALID < R: bit i set if load i has a chunk to fetch
 
   __device__ __forceinline__ void init(long ld, int mn0, int lim, int wave, int lane) {
+    live = 0;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int inst = wave * PER_WAVE + i;
@@ -119,16 +125,17 @@ struct DirectOperand {
         const int unit = (lane % ROW_UNITS) ^ (2 * tsw(k));
         const int col = min(mn0 + unit * 8, lim - 8);
         off[i] = (uint32_t)((long)k * ld + col);
+        if (unit * 8 < VALID) live |= 1u << i;
       }
     }
   }
   // base: operand origin advanced to the tile's first k
   __device__ __forceinline__ void issue(const bf16_t* base, uint4* lds, int wave) const {
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) load_lds16(base, off[i] * 2u, lds + (wave * PER_WAVE + i) * 64);
+    for (int i = 0; i < PER_WAVE; ++i) issue_one(base, lds, wave, i);
   }
   __device__ __forceinline__ void issue_one(const bf16_t* base, uint4* lds, int wave, int i) const {
-    load_lds16(base, off[i] * 2u, lds + (wave * PER_WAVE + i) * 64);
+    if (VALID == R || ((live >> i) & 1u)) load_lds16(base, off[i] * 2u, lds + (wave * PER_WAVE + i) * 64);
   }
   __device__ __forceinline__ static const bf16_t* advance(const bf16_t* base, long ld, int k) {
     return KMAJ ? base + k : base + (long)k * ld;
@@ -157,6 +164,15 @@ struct DirectOperand {
   }
 };
 
+// Width of the LDS layout of a B tile. An N-contiguous B tile of 192 columns
+// is laid out as 256 (a 384-byte row fits neither the whole-rows-per-load-
+// instruction mapping nor the segment swizzle); only its 192 columns are
+// loaded and read.
+template <bool BKM, int BN>
+__host__ __device__ constexpr int b_load_cols() {
+  return (!BKM && BN == 192) ? 256 : BN;
+}
+
 // One output tile: linear tile index L (ordered by tile_coords), split-K
 // piece `split`, batch z. LDS buffers are passed in (two per operand).
 // EPI_SK_PART: K range [kb_, ke_) and the fp32 fragment goes to skdst as a
@@ -177,7 +193,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BK = 64;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;
   using OA = DirectOperand<AK, BM, NT>;
-  using OB = DirectOperand<BKM, BN, NT>;
+  using OB = DirectOperand<BKM, b_load_cols<BKM, BN>(), NT, BN>;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -363,7 +379,10 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
       constexpr int C16 = BN / 8;            // 16-byte chunks per staged row
       constexpr int PR2 = 2 * Cfg::WM * 32;  // rows staged per pass
       constexpr int PER2 = PR2 * C16 / NT;   // chunks per thread and pass
-      static_assert((C16 & (C16 - 1)) == 0 && (PR2 * C16) % NT == 0, "bf16 staging layout");
+      // (XOR with a mask below the largest power of two dividing C16 keeps a
+      // chunk inside its row)
+      constexpr int XM = (C16 & (C16 - 1)) == 0 ? C16 - 1 : (C16 % 16 == 0 ? 15 : 7);
+      static_assert(C16 % (XM + 1) == 0 && (PR2 * C16) % NT == 0, "bf16 staging layout");
       static_assert(PR2 * BN * 2 <= 2 * (BM + BN) * 128, "staging must fit the operand buffers");
       __syncthreads();  // every wave is past its last fragment read and LDS load
       unsigned char* const st8 = reinterpret_cast<unsigned char*>(sa0);
@@ -402,7 +421,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
                 }
               }
               const f32x4_t x = {v[0], v[1], v[2], v[3]};
-              *reinterpret_cast<bf16x4_t*>(st8 + rl * (BN * 2) + (((cb >> 3) ^ (rl & (C16 - 1))) << 4) + 8 * g) =
+              *reinterpret_cast<bf16x4_t*>(st8 + rl * (BN * 2) + (((cb >> 3) ^ (rl & XM)) << 4) + 8 * g) =
                   __builtin_convertvector(x, bf16x4_t);
             }
         }
@@ -418,7 +437,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
           const int h = rs / (Cfg::WM * 32), r = rs - h * (Cfg::WM * 32);
           row = m0 + (r >> 5) * WTM + (2 * pp + h) * 32 + (r & 31);
           col = n0 + 8 * q;
-          return *reinterpret_cast<const uint4*>(st8 + rs * (BN * 2) + ((q ^ (rs & (C16 - 1))) << 4));
+          return *reinterpret_cast<const uint4*>(st8 + rs * (BN * 2) + ((q ^ (rs & XM)) << 4));
         };
         if (full) {
           // whole tile: no guards; one LDS read ahead of each store (a
@@ -467,12 +486,18 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
   __syncthreads();  // every wave is past its last fragment read and LDS load
   float4* stage = reinterpret_cast<float4*>(sa0);
   const int r32 = lane & 31, g = lane >> 5;
-  // Bias epilogues: a thread's chunks all sit in the same 8 columns (NT is a
-  // multiple of the chunks per row), so their bias is loaded once, here,
-  // rather than once per chunk behind each chunk's LDS read.
-  constexpr bool PRE_BIAS = (EPI == EPI_BIAS_SPLIT || EPI == EPI_BIAS_GELU) && NT % C8 == 0;
-  float bpre[PRE_BIAS ? 8 : 1];
-  if constexpr (PRE_BIAS) loadv<bf16_t, 8>(static_cast<const bf16_t*>(p.bias) + min(n0 + 8 * (tid % C8), p.N - 8), bpre);
+  // Bias epilogues: the bias of a thread's chunks is loaded once, here, rather
+  // than once per chunk behind each chunk's LDS read. Chunk k of a thread sits
+  // in the same 8 columns in every pass; when NT is a multiple of the chunks
+  // per row, all of a thread's chunks do (one set, else PER).
+  constexpr bool PRE_BIAS = EPI == EPI_BIAS_SPLIT || EPI == EPI_BIAS_GELU;
+  constexpr int NBQ = PRE_BIAS ? (NT % C8 == 0 ? 1 : PER) : 1;
+  float bia[NBQ][8];
+  if constexpr (PRE_BIAS) {
+#pragma unroll
+    for (int k = 0; k < NBQ; ++k)
+      loadv<bf16_t, 8>(static_cast<const bf16_t*>(p.bias) + min(n0 + 8 * ((tid + k * NT) % C8), p.N - 8), bia[k]);
+  }
 #pragma unroll
   for (int ps = 0; ps < TM; ++ps) {
     const int rl = wm * 32 + r32;
@@ -521,7 +546,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
         const int row = m0 + rt, col = n0 + 8 * q;
         if (row < p.M && col < p.N) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += bpre[e];
+          for (int e = 0; e < 8; ++e) v[e] += bia[NBQ == 1 ? 0 : k][e];
           if constexpr (EPI == EPI_BIAS_GELU) {
             float gv[8];
 #pragma unroll
@@ -556,7 +581,7 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
 template <class Cfg, bool AK, bool BKM, int EPI, typename TO, int ROLE, int KSEG = 1>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NT / 256, Cfg::NT / 256)))
 gemm_direct_kernel(const GemmArgs p) {
-  TPL_DIRECT_LDS(Cfg::BM, Cfg::BN)
+  TPL_DIRECT_LDS(Cfg::BM, (b_load_cols<BKM, Cfg::BN>()))
   direct_tile<Cfg, AK, BKM, EPI, TO, KSEG>(p, blockIdx.x, blockIdx.y, blockIdx.z, sa0, sb0, sa1, sb1);
 }
 

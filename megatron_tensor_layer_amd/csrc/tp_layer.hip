@@ -177,6 +177,7 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 // Tile configurations.
 using CfgBig = TileCfg<bf16_t, 256, 256, 2, 2>;  // linear GEMMs
 using CfgB192 = TileCfg<bf16_t, 192, 256, 2, 2>;  // linear GEMMs of one partial wave
+using CfgN192 = TileCfg<bf16_t, 256, 192, 2, 2>;  // linear GEMMs that 192-column tiles fill in whole waves
 using CfgHalf = TileCfg<bf16_t, 256, 128, 2, 2>;              // the columns past whole waves
 using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
 using CfgF32 = TileCfg<float, 64, 64, 2, 2>;     // fp32 configuration
@@ -595,6 +596,15 @@ long whole_wave_cols(const GemmArgs& p) {
   return n1;
 }
 
+// 256 x 192 tiles, when they fill one or two whole waves of the 256 CUs and
+// 256 x 256 tiles do not (a partial last wave, or stream-K fragments and a
+// fix-up). With more waves the stream-K plan of 256 x 256 tiles is faster
+// (a 256 x 192 K step costs ~0.9 of a 256 x 256 one for 0.75 of its work).
+bool n192_fills(const GemmArgs& p) {
+  const long t256 = cdivl(p.M, 256) * cdivl(p.N, 256), t192 = cdivl(p.M, 256) * cdivl(p.N, 192);
+  return p.N % 192 == 0 && p.K % 64 == 0 && !p.resid && t256 % 256 != 0 && t192 % 256 == 0 && t192 <= 512;
+}
+
 // Linear (weight) GEMM M x N x K: split-K chosen for the bf16 path.
 template <bool AK, bool BKM, int EPI, int ROLE>
 hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
@@ -602,6 +612,18 @@ hipError_t linear(const Dims& D, GemmArgs p, float* part, hipStream_t st) {
   prof::Scope sc(ROLE, 2.0 * p.M * p.N * p.K,
                  (double)D.es * ((double)p.M * p.K + (double)p.K * p.N + (1.0 + extra) * p.M * p.N), st);
   if (D.dt == TP_BF16) {
+    if constexpr (AK && !BKM && (EPI == EPI_LINEAR || EPI == EPI_BIAS_GELU)) {
+      if (n192_fills(p)) {
+        p.tiles_m = cdiv(p.M, CfgN192::BM);
+        p.tiles_n = cdiv(p.N, CfgN192::BN);
+        if (p.group_m <= 0) p.group_m = 8;
+        if (p.zdiv <= 0) p.zdiv = 1;
+        p.splits = 1;
+        hipLaunchKernelGGL((gemm_direct_kernel<CfgN192, AK, BKM, EPI, bf16_t, ROLE, 1>),
+                           dim3(p.tiles_m * p.tiles_n, 1, 1), dim3(CfgN192::NT), 0, st, p);
+        return hipGetLastError();
+      }
+    }
     SkPlan s = sk_plan(p.M, p.N, p.K);
     if (s.units) {
       s.part = part;

@@ -31,7 +31,7 @@ def _need_gpu(gpu):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("ak,bk", [(1, 0), (1, 1), (0, 0), (0, 1)])
-@pytest.mark.parametrize("M,N,K", [(272, 400, 336), (16, 32, 48), (528, 256, 1040), (528, 520, 256)])
+@pytest.mark.parametrize("M,N,K", [(272, 400, 336), (16, 32, 48), (528, 256, 1040), (528, 528, 256)])
 @pytest.mark.parametrize("alpha,with_bias", [(0.5, True), (1.0, False)])  # scaled + bias, and the plain epilogue
 def test_gemm_layouts(dtype, ak, bk, M, N, K, alpha, with_bias):
     print(f"gemm {dtype} ak={ak} bk={bk} {M}x{N}x{K} alpha={alpha} bias={with_bias}", flush=True)
@@ -56,8 +56,8 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K, alpha, with_bias):
 
 # Launch plans at full size: stream-K over a partial last wave (with and
 # without whole waves before it, ragged M and N, 3 and 6 fragments per tile,
-# with and without the per-XCD placement of stream-K tiles)
-# and split-K. Rows sampled (first, last, scattered), every column, fp64
+# with and without the per-XCD placement of stream-K tiles), whole waves of
+# 256 x 192 tiles, and split-K. Rows sampled (first, last, scattered), every column, fp64
 # reference from the same bf16 operands; a second call must match bitwise.
 @pytest.mark.parametrize("M,N,K,ak,bk,plan", [
     (2064, 4624, 12288, 1, 0, "sk"),   # 171 tiles < one wave: all stream-K (c = 129 of 192 iterations)
@@ -66,13 +66,16 @@ def test_gemm_layouts(dtype, ak, bk, M, N, K, alpha, with_bias):
     (1936, 4112, 12288, 1, 1, "dp192"),  # ragged M in 192-row tiles (1936 = 10 x 192 + 16)
     (1936, 4112, 12288, 0, 1, "dp"),     # M-contiguous A: 256-row tiles only
     (2048, 6144, 2048, 1, 1, "dp"),    # 192 tiles, one partial wave: 256 more 192-row tiles would not fit
-    (2048, 12288, 1536, 1, 0, "dp+half"),  # the 175B O projection: 256 tiles, then 8192.. as 256 x 128 tiles
+    (2048, 12288, 1536, 1, 1, "dp+half"),  # 384 tiles: 256 whole, then columns 8192.. as 256 x 128 tiles
     (2048, 10256, 1536, 1, 1, "dp+half"),  # 328 tiles: 8192 columns whole, 2064 (ragged) in 136 half tiles
     (2048, 12288, 1536, 0, 0, "dp+half"),  # M-contiguous A and N-contiguous B in the half tiles
     (2048, 10256, 1536, 0, 1, "dp+half"),
-    (2048, 6144, 12288, 1, 0, "sk"),   # the 175B FC1 shape: stream-K tiles placed as 2 x 12 blocks per XCD
+    (2048, 6144, 12288, 1, 1, "sk"),   # stream-K tiles placed as 2 x 12 blocks per XCD
     (2048, 6128, 12288, 1, 1, "sk"),   # the same placement with a ragged last tile-column
-    (2048, 12288, 6144, 1, 0, "sk"),   # the 175B FC2 shape: a whole wave, then stream-K tiles in 4 x 4 blocks
+    (2048, 12288, 6144, 1, 1, "sk"),   # a whole wave, then stream-K tiles in 4 x 4 blocks
+    (2048, 6144, 12288, 1, 0, "n192"),  # the 175B FC1 shape: one whole wave of 256 x 192 tiles
+    (2048, 12288, 6144, 1, 0, "n192"),  # the 175B FC2 shape: two whole waves of 256 x 192 tiles
+    (2048, 12288, 1536, 1, 0, "n192"),  # the 175B O projection
     (1024, 12288, 8192, 0, 1, "sk"),   # 4 tile-rows: 2 x 12 blocks per XCD, two blocks down the rows
     (2048, 10240, 4096, 1, 1, "sk"),   # a whole wave, then 64 stream-K tiles in 2 x 4 blocks from column 32
     (2064, 8208, 6144, 0, 0, "sk"),    # 297 tiles: one whole wave + stream-K over 41 tiles (6 fragments each)
@@ -90,7 +93,9 @@ def test_gemm_launch_plans_full_size(M, N, K, ak, bk, plan):
     Bd = torch.from_numpy(np.ascontiguousarray(B.T) if bk else B).to("cuda", bf)
     bd = torch.from_numpy(bias).to("cuda", bf)
     # stream-K and split-K keep fp32 partials in the workspace; whole tiles need none
-    assert (tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K) > 0) == (not plan.startswith("dp"))
+    # (the size is layout-blind: shapes that 256 x 192 tiles fill get the stream-K size)
+    if plan != "n192":
+        assert (tp.tp_gemm_workspace_bytes(tp.TP_BF16, M, N, K) > 0) == (not plan.startswith("dp"))
     outs = []
     for _ in range(2):
         C = torch.full((M, N), float("nan"), device="cuda", dtype=bf)
