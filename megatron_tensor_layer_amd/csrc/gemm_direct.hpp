@@ -393,6 +393,49 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& p, int L, int split,
       // per-element selects and guarded bias loads of the general form)
       const bool plain = p.alpha == 1.0f && !p.bias;
       const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+      // Whole tile, no scale or bias: every wave stages its own WTM x WTN
+      // block in a region of its own and stores it from there, with no
+      // further barrier (LDS operations of one wave complete in order).
+      // Row r of a wave's block is WTN * 2 bytes, its 16-byte chunk q at
+      // q ^ (r mod 16); a read instruction takes whole row segments.
+      constexpr int WC = WTN / 8;  // 16-byte chunks per row of a wave's block
+      if constexpr (WTM * WTN * 2 * (NT / 64) <= 2 * (BM + BN) * 128 && WC % 16 == 0) {
+        if (plain && full) {
+          unsigned char* const wst = st8 + wave * (WTM * WTN * 2);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                const int r = i * 32 + r32;
+                float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
+                const f32x4_t x = {v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<bf16x4_t*>(wst + r * (WTN * 2) + (((4 * j + jj) ^ (r & 15)) << 4) + 8 * g) =
+                    __builtin_convertvector(x, bf16x4_t);
+              }
+          constexpr int RPI = 64 / WC;             // rows per read instruction
+          constexpr int NRD = WTM * WC / 64;       // reads (and stores) per lane
+          const int q = lane % WC, rq = lane / WC;
+          bf16_t* const Cw = C + (long)(m0 + wm * WTM) * p.ldc + n0 + wn * WTN + 8 * q;
+          auto rd = [&](int k) {
+            const int r = k * RPI + rq;
+            return *reinterpret_cast<const uint4*>(wst + r * (WTN * 2) + ((q ^ (r & 15)) << 4));
+          };
+          uint4 x = rd(0);
+#pragma unroll
+          for (int k = 0; k < NRD; ++k) {
+            uint4 x1;
+            if (k + 1 < NRD) x1 = rd(k + 1);
+            *reinterpret_cast<uint4*>(Cw + (long)(k * RPI + rq) * p.ldc) = x;
+            __builtin_amdgcn_sched_barrier(0);
+            x = x1;
+          }
+          return;
+        }
+      }
       auto write_pass = [&](int pp, auto general) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
