@@ -176,7 +176,7 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Tile configurations.
 using CfgBig = TileCfg<bf16_t, 256, 256, 2, 2>;  // linear GEMMs
-using CfgB192 = TileCfg<bf16_t, 192, 256, 2, 2>;  // linear GEMMs of one partial wave
+using CfgB192 = TileCfg<bf16_t, 192, 256, 2, 4>;  // linear GEMMs of one partial wave (8 waves: 2 per SIMD)
 using CfgN192 = TileCfg<bf16_t, 256, 192, 2, 2>;  // linear GEMMs that 192-column tiles fill in whole waves
 using CfgHalf = TileCfg<bf16_t, 256, 128, 2, 2>;              // the columns past whole waves
 using CfgMid = TileCfg<bf16_t, 128, 128, 2, 2>;  // attention products
